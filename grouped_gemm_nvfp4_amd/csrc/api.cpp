@@ -1,0 +1,229 @@
+// api.cpp -- the C ABI declared in include/nvfp4.h.
+//
+// Host only: argument checks, the tile plan (per-group tile counts and their
+// exclusive prefix), the by-value kernel-argument table and the launch.  The
+// argument checks run before any HIP call, so they can be exercised on a
+// machine without a GPU.
+#include "nvfp4.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+using nvfp4::GemmDesc;
+using nvfp4::GroupTable;
+using nvfp4::kMaxGroupsPerLaunch;
+using nvfp4::TileConfig;
+
+// K beyond this would let a tile's buffer offsets leave the 31-bit range the
+// kernels' buffer loads use.
+constexpr int kMaxK = 1 << 24;
+// Workgroups per launch: gridDim.x * 256 threads must fit in 32 bits.
+constexpr long long kMaxWorkgroups = (0xffffffffll / 256);
+
+bool empty_output(const nvfp4_problem &p) { return p.M == 0 || p.N == 0; }
+
+nvfp4_status check_problem(const nvfp4_problem &p)
+{
+    if (p.M < 0 || p.N < 0 || p.K < 0)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (p.K % 32 != 0 || p.K > kMaxK)
+        return NVFP4_ERROR_NOT_SUPPORTED;
+    if (empty_output(p))
+        return NVFP4_OK;
+    if (p.C == nullptr)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (p.K > 0) {
+        if (!p.A || !p.SFA || !p.B || !p.SFB)
+            return NVFP4_ERROR_INVALID_VALUE;
+        if ((((uintptr_t)p.A) | ((uintptr_t)p.B)) & 15)
+            return NVFP4_ERROR_NOT_SUPPORTED; // packed operands: 16-byte aligned
+    }
+    return NVFP4_OK;
+}
+
+struct Plan {
+    TileConfig cfg;
+    int tile_m, tile_n, split_k;
+    std::vector<int> prefix; // per input group, num_groups + 1 entries
+    long long total_tiles;
+};
+
+TileConfig choose_config(const nvfp4_problem *, int) { return nvfp4::kTile128x128; }
+
+nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan)
+{
+    if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (num_groups > 0 && problems == nullptr)
+        return NVFP4_ERROR_INVALID_VALUE;
+    for (int g = 0; g < num_groups; ++g) {
+        nvfp4_status s = check_problem(problems[g]);
+        if (s != NVFP4_OK)
+            return s;
+    }
+    plan->cfg = choose_config(problems, num_groups);
+    const nvfp4::TileShape ts = nvfp4::tile_shape(plan->cfg);
+    plan->tile_m = ts.tile_m;
+    plan->tile_n = ts.tile_n;
+    plan->split_k = 1;
+    plan->prefix.assign(num_groups + 1, 0);
+    long long total = 0;
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        long long t = 0;
+        if (!empty_output(p))
+            t = (long long)((p.M + ts.tile_m - 1) / ts.tile_m) *
+                (long long)((p.N + ts.tile_n - 1) / ts.tile_n);
+        total += t;
+        if (total * plan->split_k > kMaxWorkgroups)
+            return NVFP4_ERROR_NOT_SUPPORTED;
+        plan->prefix[g + 1] = (int)total;
+    }
+    plan->total_tiles = total;
+    return NVFP4_OK;
+}
+
+void fill_info(const Plan &plan, nvfp4_plan_info *info)
+{
+    info->kernel = plan.total_tiles > 0 ? (plan.split_k > 1 ? 2 : 1) : 0;
+    info->tile_m = plan.tile_m;
+    info->tile_n = plan.tile_n;
+    info->split_k = plan.split_k;
+    info->total_tiles = (int)plan.total_tiles;
+    info->workgroups = (int)(plan.total_tiles * plan.split_k);
+    info->workspace_bytes = 0;
+}
+
+nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
+{
+    Plan plan;
+    nvfp4_status s = make_plan(problems, num_groups, &plan);
+    if (s != NVFP4_OK || plan.total_tiles == 0)
+        return s;
+
+    GroupTable table;
+    memset(&table, 0, sizeof(table));
+    table.split_k = plan.split_k;
+    int n = 0;
+    auto flush = [&]() -> nvfp4_status {
+        if (n == 0)
+            return NVFP4_OK;
+        table.num_groups = n;
+        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, nullptr, stream);
+        n = 0;
+        table.prefix[0] = 0;
+        return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
+    };
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        const int tiles = plan.prefix[g + 1] - plan.prefix[g];
+        if (tiles == 0)
+            continue;
+        GemmDesc &d = table.g[n];
+        d.A = (const uint8_t *)p.A;
+        d.SFA = (const uint8_t *)p.SFA;
+        d.B = (const uint8_t *)p.B;
+        d.SFB = (const uint8_t *)p.SFB;
+        d.C = (uint16_t *)p.C;
+        d.M = p.M;
+        d.N = p.N;
+        d.K = p.K;
+        d.tiles_m = (p.M + plan.tile_m - 1) / plan.tile_m;
+        table.prefix[n + 1] = table.prefix[n] + tiles;
+        ++n;
+        if (n == kMaxGroupsPerLaunch) {
+            s = flush();
+            if (s != NVFP4_OK)
+                return s;
+        }
+    }
+    return flush();
+}
+
+} // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const void *SFB,
+                        void *C, int M, int N, int K, hipStream_t stream)
+{
+    nvfp4_problem p;
+    p.A = A;
+    p.SFA = SFA;
+    p.B = B;
+    p.SFB = SFB;
+    p.C = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    return run(&p, 1, stream);
+}
+
+nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
+{
+    return run(problems, num_groups, stream);
+}
+
+nvfp4_status nvfp4_gemm_plan(int M, int N, int K, nvfp4_plan_info *info)
+{
+    if (info == nullptr)
+        return NVFP4_ERROR_INVALID_VALUE;
+    nvfp4_problem p;
+    memset(&p, 0, sizeof(p));
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    // pointers are not looked at: give the checks aligned non-null stand-ins
+    p.A = p.B = p.SFA = p.SFB = (const void *)(uintptr_t)256;
+    p.C = (void *)(uintptr_t)256;
+    Plan plan;
+    nvfp4_status s = make_plan(&p, 1, &plan);
+    if (s == NVFP4_OK)
+        fill_info(plan, info);
+    return s;
+}
+
+nvfp4_status nvfp4_group_gemm_plan(const nvfp4_problem *problems, int num_groups,
+                                   nvfp4_plan_info *info, int *tile_prefix)
+{
+    if (info == nullptr)
+        return NVFP4_ERROR_INVALID_VALUE;
+    Plan plan;
+    nvfp4_status s = make_plan(problems, num_groups, &plan);
+    if (s != NVFP4_OK)
+        return s;
+    fill_info(plan, info);
+    if (tile_prefix)
+        for (int g = 0; g <= num_groups; ++g)
+            tile_prefix[g] = plan.prefix[g];
+    return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_release_workspaces(void) { return NVFP4_OK; }
+
+const char *nvfp4_status_string(nvfp4_status status)
+{
+    switch (status) {
+    case NVFP4_OK:
+        return "NVFP4_OK";
+    case NVFP4_ERROR_INVALID_VALUE:
+        return "NVFP4_ERROR_INVALID_VALUE: null pointer, negative size or bad group count";
+    case NVFP4_ERROR_NOT_SUPPORTED:
+        return "NVFP4_ERROR_NOT_SUPPORTED: K must be a multiple of 32 (at most 2^24), packed "
+               "operands 16-byte aligned, tile count within range";
+    case NVFP4_ERROR_LAUNCH:
+        return "NVFP4_ERROR_LAUNCH: a HIP launch or allocation failed";
+    }
+    return "unknown nvfp4_status";
+}
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+} // extern "C"

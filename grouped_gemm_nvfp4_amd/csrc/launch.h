@@ -1,0 +1,61 @@
+// launch.h -- what the host side hands the gfx950 kernels.
+//
+// Internal to the library: shared by the C-ABI layer (api.cpp) and the
+// kernels (kernels.hip).  Everything travels to the device by value in the
+// kernel-argument segment, so a launch needs no host-to-device copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// One problem as the kernels see it.
+struct GemmDesc {
+    const uint8_t *A;   // [M][K/2] packed e2m1, low nibble = even k
+    const uint8_t *SFA; // [M][K/16] e4m3
+    const uint8_t *B;   // [N][K/2]
+    const uint8_t *SFB; // [N][K/16]
+    uint16_t *C;        // [M][N] binary16
+    int M, N, K;
+    int tiles_m;        // ceil(M / tile_m)
+};
+
+// Groups per launch.  The table below stays under the 4 KiB kernel-argument
+// budget; a call with more groups is issued as several launches.
+constexpr int kMaxGroupsPerLaunch = 64;
+
+// Exclusive prefix over per-group tile counts: workgroup w (< prefix[n]) works
+// on group g with prefix[g] <= w < prefix[g+1].
+struct GroupTable {
+    int num_groups;
+    int split_k;                         // K slices per tile (1: no split)
+    int prefix[kMaxGroupsPerLaunch + 1]; // in output tiles
+    GemmDesc g[kMaxGroupsPerLaunch];
+};
+
+// Tile configurations the kernels are built for.
+enum TileConfig : int {
+    kTile128x128 = 0, // 4 waves, 2x2 of 64x64 wave tiles
+};
+
+struct TileShape {
+    int tile_m, tile_n, tile_k;
+};
+
+inline TileShape tile_shape(TileConfig c)
+{
+    switch (c) {
+    case kTile128x128:
+    default:
+        return {128, 128, 128};
+    }
+}
+
+// Launches one grouped pass (table already filled, prefix included).  The
+// workspace, when split_k > 1, holds the fp32 partials and the per-tile
+// arrival counters (zero on entry, left zero on exit).
+hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace,
+                          hipStream_t stream);
+
+} // namespace nvfp4

@@ -1,0 +1,134 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled GEMM library.
+ *
+ * The operation (kernelbot pages nvfp4-group-gemm-498453 and nvfp4-gemm-125598,
+ * `custom_kernel` docstrings and the block-scaled MMA loop: C = A * SFA * B * SFB
+ * with sf_vec_size 16):
+ *
+ *     C[m][n] = fp16_rne( sum_{k<K} (A[m][k] * SFA[m][k/16]) * (B[n][k] * SFB[n][k/16]) )
+ *
+ * accumulated in fp32 (the pages' Float32 accumulator) and rounded to binary16
+ * with round-to-nearest-even (the raw-CUDA page nvfp4-group-gemm-407526, epilogue,
+ * `__floats2half2_rn`).  Overflow gives +-inf.
+ *
+ * Operand layouts (all dense, row-major, device memory, caller-owned):
+ *   A   [M][K/2]   uint8: two FP4 E2M1 codes per byte along K, the LOW nibble
+ *                  holds the even k (torch float4_e2m1fn_x2 of shape [M, K/2]).
+ *   SFA [M][K/16]  uint8: FP8 E4M3 ("fn": bias 7, max 448, no inf) scale codes,
+ *                  one per 16 consecutive K elements of a row.
+ *   B   [N][K/2]   uint8, SFB [N][K/16] uint8: the same for the second operand
+ *                  (B is stored N-major, K contiguous, as on the pages).
+ *   C   [M][N]     IEEE binary16, written in full by the call.
+ * A and B must be 16-byte aligned (the kernels move them in 16-byte loads);
+ * SFA, SFB and C need only their natural alignment.  C must not alias any
+ * input.
+ *
+ * Calls are asynchronous on `stream` (NULL = the device's null stream): C is
+ * valid once the stream has reached the call.  The calling thread's current
+ * HIP device must own every buffer.  Nothing is printed; no exception crosses
+ * the boundary.  Argument errors are reported before any HIP call is made.
+ *
+ * Threads: the calls may be made from several threads.  Calls that split K
+ * use a device workspace that the library keeps per (device, stream) pair and
+ * grows on demand (hipMalloc, outside the enqueued work); calls on one stream
+ * are ordered by that stream, so they never share a workspace concurrently.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+/* Largest number of groups a single grouped call accepts. */
+#define NVFP4_MAX_GROUPS 4096
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERROR_INVALID_VALUE = 1, /* null pointer, negative size, bad group count */
+    NVFP4_ERROR_NOT_SUPPORTED = 2, /* K not a multiple of 32, sizes beyond int32 tiling */
+    NVFP4_ERROR_LAUNCH = 3,        /* a HIP call failed (launch, workspace allocation) */
+} nvfp4_status;
+
+/* One independent product of a grouped call. */
+typedef struct {
+    const void *A;   /* [M][K/2] packed e2m1 */
+    const void *SFA; /* [M][K/16] e4m3 */
+    const void *B;   /* [N][K/2] packed e2m1 */
+    const void *SFB; /* [N][K/16] e4m3 */
+    void *C;         /* [M][N] binary16 */
+    int M, N, K;
+} nvfp4_problem;
+
+/*
+ * Single NVFP4 GEMM (the single-GEMM page nvfp4-gemm-125598, `custom_kernel`,
+ * with its batch size l fixed at 1).
+ *   M, N >= 0; K >= 0 and K % 32 == 0.  M == 0 or N == 0: nothing is done.
+ *   K == 0: C is filled with +0 (the empty sum).
+ * Errors: any pointer NULL while M*N > 0 (A/SFA/B/SFB only when K > 0)
+ *   -> NVFP4_ERROR_INVALID_VALUE; negative sizes -> INVALID_VALUE;
+ *   K % 32 != 0, K > 2^24, A or B not 16-byte aligned, or more than
+ *   2^24 - 1 workgroups -> NVFP4_ERROR_NOT_SUPPORTED;
+ *   a failed launch or workspace allocation -> NVFP4_ERROR_LAUNCH.
+ */
+nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const void *SFB,
+                        void *C, int M, int N, int K, hipStream_t stream);
+
+/*
+ * Grouped NVFP4 GEMM: num_groups independent products in one launch (the
+ * grouped pages nvfp4-group-gemm-407526 `group_gemm` and
+ * nvfp4-group-gemm-498453 `custom_kernel`: per-group A, B, C, SFA, SFB and
+ * (m, n, k, l) with l = 1).  Work is scheduled by an exclusive prefix sum over
+ * the groups' output-tile counts; a workgroup finds its group by searching that
+ * prefix (the CuTeDSL grouped page, group lookup from the CTA index).
+ *   `problems` is a host array of num_groups entries, read during the call only.
+ *   Up to 64 non-empty groups go into one launch; more are issued as several
+ *   launches on the same stream.
+ *   0 <= num_groups <= NVFP4_MAX_GROUPS; num_groups == 0 is a no-op.
+ *   Each group obeys the single-GEMM rules above (empty groups are skipped).
+ * Errors: as nvfp4_gemm, per group; problems == NULL with num_groups > 0 or
+ *   num_groups outside [0, NVFP4_MAX_GROUPS] -> NVFP4_ERROR_INVALID_VALUE.
+ *   On an argument error nothing is launched for any group.
+ */
+nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups,
+                              hipStream_t stream);
+
+/* How a call would be carried out (host only, no HIP call).  For tests and
+ * reports. */
+typedef struct {
+    int kernel;      /* 0: nothing to launch, 1: tiled kernel, 2: K-split kernel */
+    int tile_m;      /* output rows per workgroup */
+    int tile_n;      /* output columns per workgroup */
+    int split_k;     /* K slices per output tile (1 = none) */
+    int total_tiles; /* output tiles over all groups */
+    int workgroups;  /* workgroups launched (total_tiles * split_k) */
+    long long workspace_bytes; /* device workspace the call needs */
+} nvfp4_plan_info;
+
+/* Plan of nvfp4_gemm with these sizes; same argument rules (pointers are not
+ * looked at).  `info` must not be NULL. */
+nvfp4_status nvfp4_gemm_plan(int M, int N, int K, nvfp4_plan_info *info);
+
+/* Plan of nvfp4_group_gemm.  `tile_prefix` (may be NULL) receives the
+ * num_groups + 1 entries of the exclusive prefix over per-group tile counts. */
+nvfp4_status nvfp4_group_gemm_plan(const nvfp4_problem *problems, int num_groups,
+                                   nvfp4_plan_info *info, int *tile_prefix);
+
+/* Frees every workspace the library holds (after synchronising its device).
+ * Optional; for callers that want the memory back before process exit. */
+nvfp4_status nvfp4_release_workspaces(void);
+
+/* Static text for a status code. */
+const char *nvfp4_status_string(nvfp4_status status);
+
+/* NVFP4_ABI_VERSION of the built library. */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

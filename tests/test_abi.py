@@ -1,0 +1,135 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/nvfp4.h declares, rejects bad arguments before touching HIP,
+and plans tiles (per-group counts and their exclusive prefix) as documented.
+No call here launches work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_gemm_nvfp4_amd as g
+from grouped_gemm_nvfp4_amd import _binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    lib = g.load()
+    names = declared_functions()
+    assert "nvfp4_gemm" in names and "nvfp4_group_gemm" in names
+    for n in names:
+        assert hasattr(lib, n), "library does not export %s" % n
+    assert sorted(b.EXPORTED) == names
+
+
+def test_abi_version():
+    assert g.abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(4):
+        assert g.status_string(s).startswith("NVFP4_")
+    assert "unknown" in g.status_string(99)
+
+
+ALIGNED = 1 << 20  # stand-in device address: never dereferenced by these calls
+
+
+@pytest.mark.parametrize("M,N,K,expect", [
+    (-1, 4, 32, b.NVFP4_ERROR_INVALID_VALUE),
+    (4, -1, 32, b.NVFP4_ERROR_INVALID_VALUE),
+    (4, 4, -32, b.NVFP4_ERROR_INVALID_VALUE),
+    (4, 4, 48, b.NVFP4_ERROR_NOT_SUPPORTED),
+    (4, 4, 16, b.NVFP4_ERROR_NOT_SUPPORTED),
+    (4, 4, (1 << 24) + 32, b.NVFP4_ERROR_NOT_SUPPORTED),
+    (1 << 30, 1 << 30, 32, b.NVFP4_ERROR_NOT_SUPPORTED),
+])
+def test_gemm_rejects_bad_sizes(M, N, K, expect):
+    assert b.raw_gemm(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, M, N, K, None) == expect
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_gemm_rejects_null_pointers(which):
+    ptrs = [ALIGNED] * 5
+    ptrs[which] = None
+    assert b.raw_gemm(*ptrs, 8, 8, 64, None) == b.NVFP4_ERROR_INVALID_VALUE
+
+
+def test_gemm_rejects_misaligned_packed_operands():
+    assert b.raw_gemm(ALIGNED + 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+    assert b.raw_gemm(ALIGNED, ALIGNED, ALIGNED + 4, ALIGNED, ALIGNED, 8, 8, 64, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+
+
+def test_empty_outputs_need_no_pointers():
+    # M == 0 or N == 0: a no-op that launches nothing, whatever the pointers
+    assert b.raw_gemm(None, None, None, None, None, 0, 5, 64, None) == b.NVFP4_OK
+    assert b.raw_gemm(None, None, None, None, None, 5, 0, 64, None) == b.NVFP4_OK
+
+
+def test_group_rejects_bad_group_counts():
+    assert b.raw_group_gemm(None, -1, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert b.raw_group_gemm(None, 3, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert b.raw_group_gemm(None, 0, None) == b.NVFP4_OK
+    arr = (b.Nvfp4Problem * 4097)()
+    assert b.raw_group_gemm(arr, 4097, None) == b.NVFP4_ERROR_INVALID_VALUE
+
+
+def test_group_bad_group_fails_whole_call():
+    arr = (b.Nvfp4Problem * 3)()
+    arr[0] = b.Nvfp4Problem(0, 0, 0, 0, 0, 0, 0, 32)      # empty: fine
+    arr[1] = b.Nvfp4Problem(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64)
+    arr[2] = b.Nvfp4Problem(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 40)
+    assert b.raw_group_gemm(arr, 3, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    arr[2] = b.Nvfp4Problem(ALIGNED, None, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64)
+    assert b.raw_group_gemm(arr, 3, None) == b.NVFP4_ERROR_INVALID_VALUE
+
+
+def ceil_div(a, d):
+    return -(-a // d)
+
+
+def test_plan_single():
+    info = g.gemm_plan(8192, 8192, 8192)
+    assert info["kernel"] in (1, 2)
+    tm, tn = info["tile_m"], info["tile_n"]
+    assert info["total_tiles"] == ceil_div(8192, tm) * ceil_div(8192, tn)
+    assert info["workgroups"] == info["total_tiles"] * info["split_k"]
+    assert g.gemm_plan(0, 10, 64)["kernel"] == 0
+
+
+def test_plan_group_prefix_is_exclusive_scan_of_tile_counts():
+    shapes = [(64, 4096, 7168), (0, 4096, 7168), (512, 4096, 7168), (1, 1, 32),
+              (384, 3072, 1536), (5, 0, 32)]
+    info, prefix = g.group_gemm_plan(shapes)
+    tm, tn = info["tile_m"], info["tile_n"]
+    counts = [0 if (M == 0 or N == 0) else ceil_div(M, tm) * ceil_div(N, tn)
+              for (M, N, _) in shapes]
+    expect = [0]
+    for c in counts:
+        expect.append(expect[-1] + c)
+    assert prefix == expect
+    assert info["total_tiles"] == expect[-1]
+
+
+def test_plan_errors_match_call_errors():
+    with pytest.raises(g.Nvfp4Error) as e:
+        g.gemm_plan(4, 4, 48)
+    assert e.value.status == b.NVFP4_ERROR_NOT_SUPPORTED
+    with pytest.raises(g.Nvfp4Error):
+        g.group_gemm_plan([(4, 4, 32), (-1, 4, 32)])
+
+
+def test_problem_struct_matches_header_layout():
+    # 5 pointers then 3 ints, natural alignment
+    assert ctypes.sizeof(b.Nvfp4Problem) == 5 * 8 + 3 * 4 + 4
+    assert b.Nvfp4Problem.M.offset == 40

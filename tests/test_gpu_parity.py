@@ -1,0 +1,229 @@
+"""GPU parity: the gfx950 library against the CPU oracle, element by element.
+
+Rule (tests/parity.py): |gpu - C16| <= 1e-3 * sum_k |a_k b_k| + ulp16(C16).
+Every output buffer is poisoned with 0xFFFF (a NaN) before the call, so an
+element the kernel fails to write shows up as a failure.  Small and medium
+shapes are compared in full; the full-size workloads are compared on sampled
+outputs (whole rows and columns at tile edges plus random entries), which the
+oracle computes one by one, and checked in full for unwritten elements.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from grouped_gemm_nvfp4_amd import inputs
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import grouped_gemm_nvfp4_amd as g
+    g.load()  # raises if the library is not built: no fallback
+    return g
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def poisoned(M, N):
+    return torch.full((M, N), -1, dtype=torch.int16, device="cuda")  # 0xFFFF
+
+
+def dev_problem(p):
+    return (to_dev(p.A), to_dev(p.SFA), to_dev(p.B), to_dev(p.SFB), poisoned(p.M, p.N))
+
+
+def bits(C):
+    return C.cpu().numpy().view(np.uint16)
+
+
+def run_gemm(lib, p):
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=p.M, N=p.N, K=p.K)
+    torch.cuda.synchronize()
+    return bits(C)
+
+
+def check_full(lib, p, what):
+    got = run_gemm(lib, p)
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+    assert_parity(got, c16, bound, what)
+    return got, c16
+
+
+def sample_positions(rng, M, N, tile=128, n_random=3000):
+    rows, cols = [], []
+    edge_rows = sorted({0, M - 1} | {min(M - 1, t) for t in range(tile - 1, M, tile)}
+                       | {min(M - 1, t + 1) for t in range(tile - 1, M, tile)})
+    edge_cols = sorted({0, N - 1} | {min(N - 1, t) for t in range(tile - 1, N, tile)}
+                       | {min(N - 1, t + 1) for t in range(tile - 1, N, tile)})
+    for r in edge_rows[:6]:
+        rows += [r] * N
+        cols += list(range(N))
+    for c in edge_cols[:6]:
+        rows += list(range(M))
+        cols += [c] * M
+    rows += list(rng.integers(0, M, n_random))
+    cols += list(rng.integers(0, N, n_random))
+    return np.array(rows), np.array(cols)
+
+
+def check_sampled(got, p, seed, what):
+    assert not np.any(got == 0xFFFF), "%s: unwritten (poisoned) outputs remain" % what
+    rng = np.random.default_rng(seed)
+    rows, cols = sample_positions(rng, p.M, p.N)
+    c16, _, bound = oracle.gemm_entries(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K, rows, cols)
+    assert_parity(got[rows, cols], c16, bound, what)
+
+
+# ------------------------------------------------------------------ single GEMM
+
+def test_workload_128x128x256(lib):
+    (p,) = inputs.draw_workload(0)
+    check_full(lib, p, "128x128x256")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 32), (17, 65, 64), (64, 64, 128), (65, 129, 96), (129, 200, 416),
+    (200, 17, 256), (256, 384, 1024), (130, 260, 2080), (1, 300, 512), (300, 1, 160),
+])
+def test_edge_shapes(lib, M, N, K):
+    p = inputs.draw_problems(2000 + M + 7 * N + K, [(M, N, K)])[0]
+    check_full(lib, p, "edge %dx%dx%d" % (M, N, K))
+
+
+def test_all_ones_gives_exactly_K(lib):
+    M, N, K = 130, 70, 7168
+    ones = inputs.Problem(M, N, K, np.full((M, K // 2), 0x22, np.uint8),
+                          np.full((M, K // 16), 0x38, np.uint8),
+                          np.full((N, K // 2), 0x22, np.uint8),
+                          np.full((N, K // 16), 0x38, np.uint8))
+    got = run_gemm(lib, ones)
+    assert np.all(got.view(np.float16) == np.float16(K))
+
+
+def test_exhaustive_decode_table(lib):
+    """All 16 e2m1 codes x all 254 finite e4m3 scales through the GEMM path:
+    row (c, s) holds code c at k = 0 with scale s; B is 1.0 at k = 0 with unit
+    scale, so C = e2m1(c) * e4m3(s), exact in fp16."""
+    K = 32
+    scales = [s for s in range(256) if (s & 0x7F) != 0x7F]
+    M = 16 * len(scales)
+    A = np.zeros((M, K // 2), np.uint8)
+    SFA = np.zeros((M, K // 16), np.uint8)
+    for i, (c, s) in enumerate((c, s) for c in range(16) for s in scales):
+        A[i, 0] = c
+        SFA[i, 0] = s
+    B = np.zeros((1, K // 2), np.uint8)
+    B[0, 0] = 0x02
+    SFB = np.full((1, K // 16), 0x38, np.uint8)
+    p = inputs.Problem(M, 1, K, A, SFA, B, SFB)
+    got, c16 = check_full(lib, p, "decode table")
+    # exact: every product e2m1 * e4m3 is representable in fp16
+    nz = (c16 & 0x7FFF) != 0
+    assert np.array_equal(got[nz], c16[nz])
+
+
+def test_k_zero_fills_zero(lib):
+    C = poisoned(33, 47)
+    lib.nvfp4_gemm(None, None, None, None, C, M=33, N=47, K=0)
+    torch.cuda.synchronize()
+    assert np.all(bits(C) == 0)
+
+
+def test_empty_output_is_noop(lib):
+    C = poisoned(4, 4)
+    lib.nvfp4_gemm(None, None, None, None, C, M=0, N=4, K=64)
+    lib.nvfp4_gemm(None, None, None, None, C, M=4, N=0, K=64)
+    torch.cuda.synchronize()
+    assert np.all(bits(C) == 0xFFFF)
+
+
+def test_deterministic(lib):
+    p = inputs.draw_problems(77, [(300, 520, 3072)])[0]
+    a = run_gemm(lib, p)
+    b = run_gemm(lib, p)
+    assert np.array_equal(a, b)
+
+
+def test_overflow_gives_infinity(lib):
+    M, N, K = 2, 3, 64
+    A = np.full((M, K // 2), 0x77, np.uint8)
+    A[1] = 0xFF
+    B = np.full((N, K // 2), 0x77, np.uint8)
+    SA = np.full((M, K // 16), 0x7E, np.uint8)
+    SB = np.full((N, K // 16), 0x7E, np.uint8)
+    p = inputs.Problem(M, N, K, A, SA, B, SB)
+    got, _ = check_full(lib, p, "overflow")
+    assert np.all(got[0] == 0x7C00) and np.all(got[1] == 0xFC00)
+
+
+@pytest.mark.parametrize("index", [1, 2])
+def test_full_size_single_workloads(lib, index):
+    (p,) = inputs.draw_workload(index)
+    got = run_gemm(lib, p)
+    check_sampled(got, p, 50 + index, inputs.WORKLOADS[index].name)
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+def run_group(lib, probs):
+    devs = [dev_problem(p) for p in probs]
+    lib.nvfp4_group_gemm([d + (p.M, p.N, p.K) for d, p in zip(devs, probs)])
+    torch.cuda.synchronize()
+    return [bits(d[4]) for d in devs]
+
+
+def test_group_small_full_compare(lib):
+    shapes = [(64, 256, 512), (0, 128, 256), (200, 130, 256), (1, 1, 32), (128, 0, 64),
+              (129, 257, 1536), (64, 256, 512)]
+    probs = inputs.draw_problems(31, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "group %d" % i)
+
+
+def test_group_single_group_matches_gemm(lib):
+    (p,) = inputs.draw_problems(32, [(192, 320, 768)])
+    (g1,) = run_group(lib, [p])
+    assert np.array_equal(g1, run_gemm(lib, p))
+
+
+def test_group_many_groups_multiple_launches(lib):
+    rng = np.random.default_rng(33)
+    shapes = [(int(rng.integers(1, 140)), int(rng.integers(1, 140)), 32 * int(rng.integers(1, 9)))
+              for _ in range(150)]
+    probs = inputs.draw_problems(34, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "many-group %d" % i)
+
+
+@pytest.mark.parametrize("index", [3, 4])
+def test_full_size_grouped_workloads(lib, index):
+    probs = inputs.draw_workload(index)
+    outs = run_group(lib, probs)
+    for gi, (p, got) in enumerate(zip(probs, outs)):
+        check_sampled(got, p, 60 + 10 * index + gi, "%s group %d" % (inputs.WORKLOADS[index].name, gi))
+
+
+def test_grouped_workload_reduced_full_compare(lib):
+    """The 8-group MoE-like shape mix with K cut to 512, compared in full."""
+    _, shapes = inputs.workload_shapes(3)
+    shapes = [(m, 4096, 512) for (m, _, _) in shapes]
+    probs = inputs.draw_problems(35, shapes)
+    outs = run_group(lib, probs)
+    for gi, (p, got) in enumerate(zip(probs, outs)):
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "moe-reduced group %d" % gi)
