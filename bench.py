@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Throughput of the NVFP4 GEMM / grouped GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
+
+One step is one call of the library (nvfp4_gemm for a single product,
+nvfp4_group_gemm for a grouped one) over one set of synthetic operands that
+already sit in device memory.  The default workload is the small-M,
+bandwidth-bound product M=64 N=7168 K=16384; ``--workload`` picks another of
+the named workloads in grouped_gemm_nvfp4_amd/inputs.py.
+
+Steps cycle over several identical copies of the operands whose total size
+exceeds the 256 MiB Infinity Cache plus the L2s, so each step reads its
+operands from HBM rather than from a cache warmed by the previous step.
+
+Prints one JSON line: TFLOPS = sum 2*M*N*K / time, the roofline of the kernel
+(algorithmic bytes or flops per launch over its mean launch duration, timed
+with HIP events on the launch stream), and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from grouped_gemm_nvfp4_amd import inputs  # noqa: E402
+
+# MI355X published dense peaks
+PEAK_HBM_GBPS = 8000.0
+PEAK_FP16_TFLOPS = 2500.0
+PEAK_FP4_TFLOPS = 10100.0
+CACHE_BYTES = 256 * 2 ** 20 + 8 * 4 * 2 ** 20  # Infinity Cache + 8 XCD L2s
+
+METRIC = "TFLOPS (2MNK/t) NVFP4 GEMM & grouped GEMM; % FP4 MFMA peak; HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1,
+                    help="index into grouped_gemm_nvfp4_amd.inputs.WORKLOADS")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="operand copies to cycle over (0: enough to exceed the caches)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0: skip)")
+    return ap.parse_args()
+
+
+def cpu_baseline(probs, target_s):
+    """Time the oracle on a bounded sample of the workload, about target_s
+    seconds of CPU work: the whole workload, repeated, when one pass is
+    shorter than that; otherwise the leading rows of each problem's A with all
+    of N and K."""
+    import oracle
+
+    total_flops = inputs.flops([(p.M, p.N, p.K) for p in probs])
+    threads = oracle.num_threads()
+
+    def run(frac):
+        flops_done, rows = 0, []
+        for p in probs:
+            m = min(p.M, max(1, int(round(p.M * frac)))) if p.M > 0 else 0
+            rows.append(m)
+            if m and p.N:
+                oracle.gemm(np.ascontiguousarray(p.A[:m]), np.ascontiguousarray(p.SFA[:m]),
+                            p.B, p.SFB, m, p.N, p.K)
+                flops_done += 2 * m * p.N * p.K
+        return flops_done, rows
+
+    # calibrate on a slice with at least one row per thread
+    frac = min(1.0, max(threads / max(1, probs[0].M), 2e9 / total_flops))
+    t0 = time.perf_counter()
+    f_cal, _ = run(frac)
+    rate = f_cal / max(1e-9, time.perf_counter() - t0)
+    frac = min(1.0, target_s * rate / total_flops)
+    reps = max(1, int(round(target_s * rate / total_flops))) if frac >= 1.0 else 1
+    done = 0
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        f, rows = run(frac)
+        done += f
+    dt = time.perf_counter() - t0
+    if frac >= 1.0:
+        sample = "the whole workload, %d pass(es), %.1f s" % (reps, dt)
+    else:
+        sample = ("leading %s rows of M (all N and K) of each problem: %.3g of the "
+                  "workload's flops, %.1f s" % (rows, done / total_flops, dt))
+    return {"value": done / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import grouped_gemm_nvfp4_amd as g
+    from grouped_gemm_nvfp4_amd import _binding as b
+
+    lib = g.load()
+    wl = inputs.WORKLOADS[args.workload]
+    probs = inputs.draw_workload(args.workload)
+    shapes = [(p.M, p.N, p.K) for p in probs]
+    flops = inputs.flops(shapes)
+    alg_bytes = inputs.algorithmic_bytes(shapes)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    copies = args.copies or max(2, int(np.ceil(2 * CACHE_BYTES / alg_bytes)) + 1)
+    copies = min(copies, 64)
+    sets = []
+    host = [[torch.from_numpy(x) for x in (p.A, p.SFA, p.B, p.SFB)] for p in probs]
+    for _ in range(copies):
+        one = []
+        for p, h in zip(probs, host):
+            A, SFA, B, SFB = (x.to(dev) for x in h)
+            C = torch.empty((p.M, p.N), dtype=torch.float16, device=dev)
+            one.append((A, SFA, B, SFB, C))
+        sets.append(one)
+
+    # marshal each set once; a step is then a single C call
+    calls = []
+    for one in sets:
+        if not wl.grouped:
+            (A, SFA, B, SFB, C), p = one[0], probs[0]
+            args_c = (A.data_ptr(), SFA.data_ptr(), B.data_ptr(), SFB.data_ptr(),
+                      C.data_ptr(), p.M, p.N, p.K, sh)
+            calls.append(("gemm", args_c))
+        else:
+            arr = (b.Nvfp4Problem * len(one))()
+            for i, ((A, SFA, B, SFB, C), p) in enumerate(zip(one, probs)):
+                arr[i] = b.Nvfp4Problem(A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
+                                        SFB.data_ptr(), C.data_ptr(), p.M, p.N, p.K)
+            calls.append(("group", (arr, len(one), sh)))
+
+    def step(i):
+        kind, a = calls[i % len(calls)]
+        rc = lib.nvfp4_gemm(*a) if kind == "gemm" else lib.nvfp4_group_gemm(*a)
+        if rc != 0:
+            raise RuntimeError(g.status_string(rc))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev0[i].record(stream)
+        step(i)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
+    kern_s = float(np.mean(launch_ms)) / 1e3
+
+    # same operands every step (cache-warm), for context only
+    torch.cuda.synchronize()
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    nwarm = min(K, 50)
+    w0.record(stream)
+    for _ in range(nwarm):
+        step(0)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_s = w0.elapsed_time(w1) / 1e3 / nwarm
+
+    value = flops * K / wall / 1e12
+    kern_tflops = flops / kern_s / 1e12
+    kern_gbps = alg_bytes / kern_s / 1e9
+    small_m = (not wl.grouped) and probs[0].M <= 128
+    if small_m:
+        roof = {"bound": "hbm", "achieved": kern_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": kern_gbps / PEAK_HBM_GBPS, "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS, "traffic": None}
+    roof["per_launch"] = {"flops": flops, "algorithmic_bytes": alg_bytes,
+                          "mean_launch_us": kern_s * 1e6,
+                          "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
+                          "p90_us": float(np.percentile(launch_ms, 90)) * 1e3}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(probs, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "shapes_MNK": shapes, "seed": 1000 + args.workload,
+                   "operand_copies": copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "pct_fp4_peak": 100.0 * kern_tflops / PEAK_FP4_TFLOPS,
+        "pct_fp16_peak": 100.0 * kern_tflops / PEAK_FP16_TFLOPS,
+        "hbm_gbps": kern_gbps,
+        "kernel_tflops": kern_tflops,
+        "warm_cache_us": warm_s * 1e6,
+        "warm_cache_tflops": flops / warm_s / 1e12,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
