@@ -10,6 +10,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "launch.h"
@@ -53,9 +56,71 @@ struct Plan {
     int tile_m, tile_n, split_k;
     std::vector<int> prefix; // per input group, num_groups + 1 entries
     long long total_tiles;
+    long long workspace_bytes;
 };
 
-TileConfig choose_config(const nvfp4_problem *, int) { return nvfp4::kTile128x128; }
+// Workspaces for K-split launches, one per (device, stream): work on one
+// stream runs in order, so a stream's calls never use its workspace
+// concurrently.  A buffer is only ever replaced by a larger one; replaced
+// buffers stay allocated (a captured graph may still refer to them) until
+// nvfp4_release_workspaces.
+struct Workspaces {
+    std::mutex mu;
+    std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> live;
+    std::vector<std::pair<int, void *>> retired;
+};
+
+Workspaces &workspaces()
+{
+    static Workspaces *w = new Workspaces(); // never destroyed: usable at exit
+    return *w;
+}
+
+nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
+{
+    *out = nullptr;
+    if (bytes == 0)
+        return NVFP4_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return NVFP4_ERROR_LAUNCH;
+    Workspaces &w = workspaces();
+    std::lock_guard<std::mutex> lock(w.mu);
+    auto &e = w.live[std::make_pair(dev, stream)];
+    if (e.first != nullptr && e.second >= bytes) {
+        *out = e.first;
+        return NVFP4_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (stream != nullptr && hipStreamIsCapturing(stream, &cs) == hipSuccess &&
+        cs != hipStreamCaptureStatusNone)
+        return NVFP4_ERROR_NOT_SUPPORTED; // cannot allocate inside a capture
+    const size_t grown = std::max(bytes, e.second + e.second / 2);
+    const size_t rounded = (grown + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);
+    void *p = nullptr;
+    if (hipMalloc(&p, rounded) != hipSuccess)
+        return NVFP4_ERROR_LAUNCH;
+    if (e.first != nullptr)
+        w.retired.emplace_back(dev, e.first);
+    e = std::make_pair(p, rounded);
+    *out = p;
+    return NVFP4_OK;
+}
+
+// Skinny tiles (64 x 256, K split across workgroups when the tiles alone
+// cannot fill the chip) when every group has M <= 64; 128 x 128 otherwise.
+TileConfig choose_config(const nvfp4_problem *problems, int num_groups)
+{
+    int max_m = 0;
+    for (int g = 0; g < num_groups; ++g)
+        if (!empty_output(problems[g]))
+            max_m = std::max(max_m, problems[g].M);
+    return (max_m > 0 && max_m <= 64) ? nvfp4::kSkinny64x256 : nvfp4::kTile128x128;
+}
+
+// Workgroups that keep every compute unit of an MI355X busy.
+constexpr int kTargetWorkgroups = 256;
+constexpr int kMaxSplitK = 16;
 
 nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan)
 {
@@ -75,18 +140,28 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     plan->split_k = 1;
     plan->prefix.assign(num_groups + 1, 0);
     long long total = 0;
+    int max_ktiles = 0;
     for (int g = 0; g < num_groups; ++g) {
         const nvfp4_problem &p = problems[g];
         long long t = 0;
-        if (!empty_output(p))
+        if (!empty_output(p)) {
             t = (long long)((p.M + ts.tile_m - 1) / ts.tile_m) *
                 (long long)((p.N + ts.tile_n - 1) / ts.tile_n);
+            max_ktiles = std::max(max_ktiles, (p.K + ts.tile_k - 1) / ts.tile_k);
+        }
         total += t;
-        if (total * plan->split_k > kMaxWorkgroups)
+        if (total > kMaxWorkgroups)
             return NVFP4_ERROR_NOT_SUPPORTED;
         plan->prefix[g + 1] = (int)total;
     }
     plan->total_tiles = total;
+    // Split K only where the kernel supports it and the tiles alone leave
+    // compute units idle: at most kTargetWorkgroups workgroups in all, so each
+    // runs once, in a single wave of workgroups.
+    if (plan->cfg == nvfp4::kSkinny64x256 && total > 0 && total * 2 <= kTargetWorkgroups)
+        plan->split_k = (int)std::min<long long>(
+            {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles), (long long)kMaxSplitK});
+    plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
     return NVFP4_OK;
 }
 
@@ -98,7 +173,7 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
     info->split_k = plan.split_k;
     info->total_tiles = (int)plan.total_tiles;
     info->workgroups = (int)(plan.total_tiles * plan.split_k);
-    info->workspace_bytes = 0;
+    info->workspace_bytes = plan.workspace_bytes;
 }
 
 nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
@@ -106,6 +181,11 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
     Plan plan;
     nvfp4_status s = make_plan(problems, num_groups, &plan);
     if (s != NVFP4_OK || plan.total_tiles == 0)
+        return s;
+
+    void *workspace = nullptr;
+    s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
+    if (s != NVFP4_OK)
         return s;
 
     GroupTable table;
@@ -116,7 +196,8 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
         if (n == 0)
             return NVFP4_OK;
         table.num_groups = n;
-        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, nullptr, stream);
+        // launches of one call share the workspace: stream order keeps them apart
+        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, workspace, stream);
         n = 0;
         table.prefix[0] = 0;
         return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
@@ -206,7 +287,30 @@ nvfp4_status nvfp4_group_gemm_plan(const nvfp4_problem *problems, int num_groups
     return NVFP4_OK;
 }
 
-nvfp4_status nvfp4_release_workspaces(void) { return NVFP4_OK; }
+nvfp4_status nvfp4_release_workspaces(void)
+{
+    Workspaces &w = workspaces();
+    std::lock_guard<std::mutex> lock(w.mu);
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return NVFP4_ERROR_LAUNCH;
+    nvfp4_status st = NVFP4_OK;
+    auto release = [&](int dev, void *p) {
+        if (hipSetDevice(dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipFree(p) != hipSuccess)
+            st = NVFP4_ERROR_LAUNCH;
+    };
+    for (auto &kv : w.live)
+        if (kv.second.first)
+            release(kv.first.first, kv.second.first);
+    for (auto &r : w.retired)
+        release(r.first, r.second);
+    w.live.clear();
+    w.retired.clear();
+    if (hipSetDevice(cur) != hipSuccess)
+        st = NVFP4_ERROR_LAUNCH;
+    return st;
+}
 
 const char *nvfp4_status_string(nvfp4_status status)
 {

@@ -37,6 +37,7 @@ struct GroupTable {
 // Tile configurations the kernels are built for.
 enum TileConfig : int {
     kTile128x128 = 0, // 4 waves, 2x2 of 64x64 wave tiles
+    kSkinny64x256 = 1, // 8 waves side by side in N; A decoded once into LDS; K may be split
 };
 
 struct TileShape {
@@ -46,15 +47,31 @@ struct TileShape {
 inline TileShape tile_shape(TileConfig c)
 {
     switch (c) {
+    case kSkinny64x256:
+        return {64, 256, 128};
     case kTile128x128:
     default:
         return {128, 128, 128};
     }
 }
 
-// Launches one grouped pass (table already filled, prefix included).  The
-// workspace, when split_k > 1, holds the fp32 partials and the per-tile
-// arrival counters (zero on entry, left zero on exit).
+// fp32 elements of one output tile's partial sum (K-split kernels).
+inline long long partial_elems(TileConfig c)
+{
+    const TileShape t = tile_shape(c);
+    return (long long)t.tile_m * t.tile_n;
+}
+
+// Device workspace one launch of `table` needs (bytes): the fp32 partial sums
+// of every (tile, K slice) when split_k > 1, else nothing.
+inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k)
+{
+    return split_k > 1 ? total_tiles * split_k * partial_elems(c) * 4 : 0;
+}
+
+// Launches one grouped pass (table already filled, prefix included).  With
+// split_k > 1 the workspace holds the partial sums; a second kernel on the
+// same stream adds them in K-slice order and writes C.
 hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace,
                           hipStream_t stream);
 

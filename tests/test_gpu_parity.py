@@ -99,6 +99,18 @@ def test_edge_shapes(lib, M, N, K):
     check_full(lib, p, "edge %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (64, 7168, 2080), (40, 1000, 1536), (64, 300, 16384), (1, 4097, 4096),
+    (63, 257, 96), (33, 513, 8192),
+])
+def test_small_m_split_k_shapes(lib, M, N, K):
+    """M <= 64 takes the skinny kernel; few tiles make it split K."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["tile_m"] == 64
+    p = inputs.draw_problems(3000 + M + N + K, [(M, N, K)])[0]
+    check_full(lib, p, "small-M %dx%dx%d split %d" % (M, N, K, info["split_k"]))
+
+
 def test_all_ones_gives_exactly_K(lib):
     M, N, K = 130, 70, 7168
     ones = inputs.Problem(M, N, K, np.full((M, K // 2), 0x22, np.uint8),
@@ -191,6 +203,24 @@ def test_group_small_full_compare(lib):
             continue
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "group %d" % i)
+
+
+def test_group_small_m_split_k(lib):
+    rng = np.random.default_rng(36)
+    shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 700)), 32 * int(rng.integers(1, 40)))
+              for _ in range(12)] + [(0, 64, 64), (64, 64, 0)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["split_k"] > 1
+    probs = inputs.draw_problems(37, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "small-M group %d" % i)
 
 
 def test_group_single_group_matches_gemm(lib):
