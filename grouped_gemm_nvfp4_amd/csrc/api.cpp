@@ -107,15 +107,16 @@ nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
     return NVFP4_OK;
 }
 
-// Skinny tiles (64 x 256, K split across workgroups when the tiles alone
-// cannot fill the chip) when every group has M <= 64; 128 x 128 otherwise.
+// Stream tiles (64 x 32, eight waves splitting K; K also split across
+// workgroups when the tiles alone cannot fill the chip) when every group has
+// M <= 64; 128 x 128 otherwise.
 TileConfig choose_config(const nvfp4_problem *problems, int num_groups)
 {
     int max_m = 0;
     for (int g = 0; g < num_groups; ++g)
         if (!empty_output(problems[g]))
             max_m = std::max(max_m, problems[g].M);
-    return (max_m > 0 && max_m <= 64) ? nvfp4::kSkinny64x256 : nvfp4::kTile128x128;
+    return (max_m > 0 && max_m <= 64) ? nvfp4::kStream64x32 : nvfp4::kTile128x128;
 }
 
 // Workgroups that keep every compute unit of an MI355X busy.
@@ -158,9 +159,10 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     // Split K only where the kernel supports it and the tiles alone leave
     // compute units idle: at most kTargetWorkgroups workgroups in all, so each
     // runs once, in a single wave of workgroups.
-    if (plan->cfg == nvfp4::kSkinny64x256 && total > 0 && total * 2 <= kTargetWorkgroups)
+    // (a slice keeps at least 4 K tiles: half a K tile per wave)
+    if (plan->cfg == nvfp4::kStream64x32 && total > 0 && total * 2 <= kTargetWorkgroups)
         plan->split_k = (int)std::min<long long>(
-            {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles), (long long)kMaxSplitK});
+            {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles / 4), (long long)kMaxSplitK});
     plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
     return NVFP4_OK;
 }

@@ -79,31 +79,54 @@ __device__ inline int find_group(const GroupTable &t, int w)
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: one workgroup of 256 threads (4 waves, 2x2) per BM x BN output
-// tile, K consumed in BK-element tiles staged through LDS, double-buffered.
+// Tiled kernel: one workgroup of a single wave per 128 x 128 output tile.
+// Four such workgroups share a CU (one per SIMD); each keeps its own LDS
+// region, so no barrier is ever needed.
+//
+// Decode cost sets the tile: every 32x32x16 MFMA (32 cycles) needs an A and a
+// B fragment of 8 elements per lane, 8 VALU instructions each (4 cvt + 4 mul,
+// 4 cycles apiece on a 16-lane SIMD).  A wave owning a 128 x 128 tile decodes
+// 4 A and 4 B fragments per 16 K and reuses them across 16 MFMAs: 4 VALU
+// instructions per MFMA, half the MFMA time, issued in its shadow.
+//
+// Per K tile (128 elements): 20 loads per lane (A and B: 128 rows x 64 bytes;
+// their 8 scale bytes per row) into registers one K tile ahead, then into the
+// LDS stage; per 64-K group the lane reads 16 packed bytes of each of its 4 A
+// rows and 4 B rows and runs 4 k-steps of 16 MFMAs.  LDS rows are 64 bytes
+// with the 16-byte chunk index XORed with (row / 4) % 4, which makes both the
+// row-wise writes and the MFMA-layout reads bank-conflict free, and keeps two
+// stages at 36 KiB so that four workgroups fit a CU's 160 KiB.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK>
-struct TiledCfg {
-    static constexpr int kThreads = 256;
-    static constexpr int kWavesM = 2, kWavesN = 2;
-    static constexpr int kWaveM = BM / kWavesM, kWaveN = BN / kWavesN;
-    static constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
-    static constexpr int kRowBytes = BK / 2;          // packed bytes per row per K tile
-    static constexpr int kStride = kRowBytes + 16;    // padded LDS row (bank spread)
-    static constexpr int kSfBytes = BK / 16;          // scale bytes per row per K tile
-    static constexpr int kStageBytes = (BM + BN) * kStride + (BM + BN) * kSfBytes;
-    static constexpr int kCStride = BN + 8;           // fp16 elements per LDS C row
-    static constexpr int kSmemBytes =
-        (2 * kStageBytes > BM * kCStride * 2) ? 2 * kStageBytes : BM * kCStride * 2;
-    static_assert(BK == 128, "scale handling below assumes 8 scale bytes per row");
-    static_assert(BM == 128 && BN == 128, "load distribution assumes 128x128");
+namespace tiled {
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int kRowBytes = BK / 2;          // 64 packed bytes per row per K tile
+constexpr int kStride = kRowBytes;         // swizzled, unpadded LDS row
+constexpr int kSfBytes = BK / 16;          // 8 scale bytes per row per K tile
+constexpr int kAOff = 0;
+constexpr int kBOff = BM * kStride;
+constexpr int kSaOff = kBOff + BN * kStride;
+constexpr int kSbOff = kSaOff + BM * kSfBytes;
+constexpr int kStageBytes = kSbOff + BN * kSfBytes; // 18432
+// byte offset of 16-byte chunk c of row r within an A or B stage
+__device__ inline int swz(int r, int c) { return r * kStride + ((c ^ ((r >> 2) & 3)) << 4); }
+constexpr int kCStride = BN * 2 + 16;      // bytes per fp16 C row in LDS
+static_assert(2 * kStageBytes >= BM * kCStride, "C tile reuses the stages");
+} // namespace tiled
+
+struct TiledSlot {
+    u32x4 a[8];   // A chunk c = 64 j + lane: row c / 4, bytes 16 (c % 4)
+    u32x4 b[8];
+    u32x2 sa[2];  // A scale rows lane and 64 + lane
+    u32x2 sb[2];
 };
 
-template <int BM, int BN, int BK>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(GroupTable tab)
+// kVec: K % 128 == 0 and both scale arrays 8-byte aligned (one 8-byte load
+// per row and K tile); otherwise 2-byte loads, pairs past K read as zero.
+template <bool kVec>
+__global__ __launch_bounds__(64) void gemm_tiled_kernel(GroupTable tab)
 {
-    using Cfg = TiledCfg<BM, BN, BK>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::kSmemBytes];
+    using namespace tiled;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
 
     const int w = blockIdx.x;
     const int gi = find_group(tab, w);
@@ -114,181 +137,146 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GroupTable tab)
     const int M = d.M, N = d.N, K = d.K;
     const int row0 = tm * BM, col0 = tn * BN;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
-    const int wm = wave / Cfg::kWavesN, wn = wave % Cfg::kWavesN;
-    const int half_id = lane >> 5; // which K half of the 64-K group
+    const int lane = threadIdx.x;
+    const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    const long kb_row = K / 2;   // packed bytes per row
-    const long ks_row = K / 16;  // scale bytes per row
+    const int kb_row = K / 2;
+    const int ks_row = K / 16;
+    const int nkt = (K + BK - 1) / BK;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
 
-    const int nk = (K + BK - 1) / BK;
-    const bool sf_vec_ok = (K % BK) == 0 &&
-                           ((((uintptr_t)d.SFA) | ((uintptr_t)d.SFB)) & 7) == 0;
+    const int crow = lane >> 2, c16 = lane & 3;
+    const uint32_t line_off = (uint32_t)(crow * kb_row + c16 * 16);
 
-    // Per-thread global load slots: 2 A chunks, 2 B chunks (16 B each) and one
-    // 8-byte scale row (threads 0..127: SFA rows, 128..255: SFB rows).
-    u32x4 ga[2], gb[2];
-    u32x2 gs;
-
-    auto load_tile = [&](int kt) {
-        const int kbyte0 = kt * Cfg::kRowBytes;
+    auto load = [&](TiledSlot &s, int kt) {
+        const bool live = kt < nkt;
+        const int kb = kt * kRowBytes, ks = kt * kSfBytes;
+        const bool cin = live && (kb + c16 * 16) < kb_row; // chunk inside K
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + i * 256;
-            const int row = c >> 2, col = c & 3;
-            const int kb = kbyte0 + col * 16;
-            const uint32_t off = (kb < kb_row) ? (uint32_t)(row * kb_row + kb) : kOutOfRange;
-            ga[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
-            gb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = cin ? line_off + (uint32_t)(16 * j * kb_row + kb) : kOutOfRange;
+            s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+            s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
         }
-        const int srow = tid & 127;
-        const __amdgpu_buffer_rsrc_t rs = (wave < 2) ? rSA : rSB; // waves 0-1: SFA rows
-        const uint32_t sbase = (uint32_t)(srow * ks_row + kt * Cfg::kSfBytes);
-        if (sf_vec_ok) {
-            gs = __builtin_amdgcn_raw_buffer_load_b64(rs, sbase, 0, 0);
-        } else {
-            // tail or unaligned: byte loads, blocks past K read as 0
-            uint32_t lo = 0, hi = 0;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const bool ok = (kt * Cfg::kSfBytes + b) < ks_row;
-                const uint32_t v = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? sbase + b : kOutOfRange, 0, 0);
-                if (b < 4)
-                    lo |= v << (8 * b);
-                else
-                    hi |= v << (8 * (b - 4));
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t row = (uint32_t)(64 * j + lane);
+            if (kVec) {
+                const uint32_t off = live ? row * ks_row + ks : kOutOfRange;
+                s.sa[j] = __builtin_amdgcn_raw_buffer_load_b64(rSA, off, 0, 0);
+                s.sb[j] = __builtin_amdgcn_raw_buffer_load_b64(rSB, off, 0, 0);
+            } else {
+                uint32_t va[4], vb[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const bool ok = live && (ks + 2 * p) < ks_row;
+                    const uint32_t off = ok ? row * ks_row + ks + 2 * p : kOutOfRange;
+                    va[p] = __builtin_amdgcn_raw_buffer_load_b16(rSA, off, 0, 0);
+                    vb[p] = __builtin_amdgcn_raw_buffer_load_b16(rSB, off, 0, 0);
+                }
+                s.sa[j] = (u32x2){va[0] | (va[1] << 16), va[2] | (va[3] << 16)};
+                s.sb[j] = (u32x2){vb[0] | (vb[1] << 16), vb[2] | (vb[3] << 16)};
             }
-            gs = (u32x2){lo, hi};
         }
     };
 
-    auto store_tile = [&](int buf) {
-        uint8_t *st = smem + buf * Cfg::kStageBytes;
-        uint8_t *sA = st;
-        uint8_t *sB = st + BM * Cfg::kStride;
-        uint8_t *sS = st + (BM + BN) * Cfg::kStride; // SFA rows then SFB rows
+    auto put = [&](const TiledSlot &s, int buf) {
+        uint8_t *st = lds + buf * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + i * 256;
-            const int row = c >> 2, col = c & 3;
-            *(u32x4 *)(sA + row * Cfg::kStride + col * 16) = ga[i];
-            *(u32x4 *)(sB + row * Cfg::kStride + col * 16) = gb[i];
+        for (int j = 0; j < 8; ++j) {
+            *(u32x4 *)(st + kAOff + swz(16 * j + crow, c16)) = s.a[j];
+            *(u32x4 *)(st + kBOff + swz(16 * j + crow, c16)) = s.b[j];
         }
-        *(u32x2 *)(sS + tid * Cfg::kSfBytes) = gs;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            *(u32x2 *)(st + kSaOff + (64 * j + lane) * kSfBytes) = s.sa[j];
+            *(u32x2 *)(st + kSbOff + (64 * j + lane) * kSfBytes) = s.sb[j];
+        }
     };
 
-    f32x16 acc[Cfg::kFragM][Cfg::kFragN];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < Cfg::kFragM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::kFragN; ++j)
+        for (int j = 0; j < 4; ++j)
             acc[i][j] = (f32x16){};
+    const uint32_t sh = h * 16;
 
-    auto compute_tile = [&](int buf) {
-        const uint8_t *st = smem + buf * Cfg::kStageBytes;
-        const uint8_t *sA = st;
-        const uint8_t *sB = st + BM * Cfg::kStride;
-        const uint8_t *sSA = st + (BM + BN) * Cfg::kStride;
-        const uint8_t *sSB = sSA + BM * Cfg::kSfBytes;
-
-        // scales: for this lane's half, blocks {2h, 2h+1} of 64-K group 0 and
-        // {4+2h, 5+2h} of group 1, as fp16 pairs
-        half2_t sa[Cfg::kFragM][2], sb[Cfg::kFragN][2];
+    // MFMA work of one 64-K group g of the tile in stage buf
+    auto compute = [&](int buf, int g) {
+        const uint8_t *st = lds + buf * kStageBytes;
+        // scale pairs of this lane's half of group g: blocks 4g+2h, 4g+2h+1
+        half2_t ca[4], cb[4];
+        u32x4 pa[4], pb[4];
 #pragma unroll
-        for (int i = 0; i < Cfg::kFragM; ++i) {
-            const u32x2 v = *(const u32x2 *)(sSA + (wm * Cfg::kWaveM + i * 32 + l32) * Cfg::kSfBytes);
-            const uint32_t sel = half_id ? ((v.x >> 16) | (v.y & 0xffff0000u))
-                                         : ((v.x & 0xffffu) | (v.y << 16));
-            sa[i][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sel, 1.0f, false);
-            sa[i][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sel, 1.0f, true);
+        for (int i = 0; i < 4; ++i) {
+            const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
+            const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
+            ca[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
+            cb[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
+            pa[i] = *(const u32x4 *)(st + kAOff + swz(32 * i + l32, 2 * g + h));
+            pb[i] = *(const u32x4 *)(st + kBOff + swz(32 * i + l32, 2 * g + h));
         }
 #pragma unroll
-        for (int j = 0; j < Cfg::kFragN; ++j) {
-            const u32x2 v = *(const u32x2 *)(sSB + (wn * Cfg::kWaveN + j * 32 + l32) * Cfg::kSfBytes);
-            const uint32_t sel = half_id ? ((v.x >> 16) | (v.y & 0xffff0000u))
-                                         : ((v.x & 0xffffu) | (v.y << 16));
-            sb[j][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sel, 1.0f, false);
-            sb[j][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sel, 1.0f, true);
-        }
-
+        for (int q = 0; q < 4; ++q) {
+            half8_t fa[4], fb[4];
 #pragma unroll
-        for (int g = 0; g < BK / 64; ++g) {
-            u32x4 pa[Cfg::kFragM], pb[Cfg::kFragN];
-#pragma unroll
-            for (int i = 0; i < Cfg::kFragM; ++i)
-                pa[i] = *(const u32x4 *)(sA + (wm * Cfg::kWaveM + i * 32 + l32) * Cfg::kStride +
-                                         g * 32 + half_id * 16);
-#pragma unroll
-            for (int j = 0; j < Cfg::kFragN; ++j)
-                pb[j] = *(const u32x4 *)(sB + (wn * Cfg::kWaveN + j * 32 + l32) * Cfg::kStride +
-                                         g * 32 + half_id * 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                half8_t fa[Cfg::kFragM], fb[Cfg::kFragN];
-#pragma unroll
-                for (int i = 0; i < Cfg::kFragM; ++i)
-                    fa[i] = decode8(pa[i][q], (q < 2) ? bcast_lo(sa[i][g]) : bcast_hi(sa[i][g]));
-#pragma unroll
-                for (int j = 0; j < Cfg::kFragN; ++j)
-                    fb[j] = decode8(pb[j][q], (q < 2) ? bcast_lo(sb[j][g]) : bcast_hi(sb[j][g]));
-#pragma unroll
-                for (int i = 0; i < Cfg::kFragM; ++i)
-#pragma unroll
-                    for (int j = 0; j < Cfg::kFragN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                fa[i] = decode8(pa[i][q], q < 2 ? bcast_lo(ca[i]) : bcast_hi(ca[i]));
+                fb[i] = decode8(pb[i][q], q < 2 ? bcast_lo(cb[i]) : bcast_hi(cb[i]));
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
     };
 
-    if (nk > 0) {
-        load_tile(0);
-        store_tile(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk)
-                load_tile(kt + 1);
-            compute_tile(cur);
-            if (kt + 1 < nk)
-                store_tile(cur ^ 1);
-            __syncthreads();
+    if (nkt > 0) {
+        TiledSlot x;
+        load(x, 0);
+        put(x, 0);
+        load(x, 1);
+        for (int kt = 0; kt < nkt; ++kt) {
+            // stage kt&1 holds tile kt; x holds tile kt + 1 (in flight).  The
+            // refill sits between the two halves so that it issues while the
+            // first half's MFMAs run.
+            compute(kt & 1, 0);
+            put(x, (kt + 1) & 1);
+            load(x, kt + 2);
+            compute(kt & 1, 1);
         }
     }
 
-    // Epilogue: fp32 -> fp16 (round to nearest even) through LDS, then
-    // row-contiguous stores masked to M x N.
-    uint16_t *sC = (uint16_t *)smem;
+    // epilogue: fp32 -> fp16 (round to nearest even) into LDS, then 16-byte
+    // row-contiguous stores masked to M x N.  The stages are free: the wave's
+    // own LDS accesses are ordered.
+    uint8_t *sC = lds;
 #pragma unroll
-    for (int i = 0; i < Cfg::kFragM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::kFragN; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = wm * Cfg::kWaveM + i * 32 + (e >> 2) * 8 + half_id * 4 + (e & 3);
-                const int col = wn * Cfg::kWaveN + j * 32 + l32;
-                sC[row * Cfg::kCStride + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
+                const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
+                const int col = 32 * j + l32;
+                *(uint16_t *)(sC + row * kCStride + col * 2) = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
             }
-    __syncthreads();
-
     const bool vec_ok = (N % 8 == 0) && ((((uintptr_t)d.C) & 15) == 0);
-    constexpr int kSegsPerRow = BN / 8;
-#pragma unroll
-    for (int s = 0; s < (BM * kSegsPerRow) / 256; ++s) {
-        const int seg = tid + s * 256;
-        const int row = seg / kSegsPerRow;
-        const int c8 = (seg % kSegsPerRow) * 8;
+#pragma unroll 4
+    for (int s = 0; s < BM * BN / 8 / 64; ++s) {
+        const int seg = s * 64 + lane;
+        const int row = seg >> 4, c8 = (seg & 15) * 8;
         const int grow = row0 + row, gcol = col0 + c8;
         if (grow >= M)
             continue;
         uint16_t *dst = d.C + (long)grow * N + gcol;
-        const uint16_t *src = sC + row * Cfg::kCStride + c8;
+        const uint16_t *src = (const uint16_t *)(sC + row * kCStride + c8 * 2);
         if (vec_ok && gcol + 8 <= N) {
             *(u32x4 *)dst = *(const u32x4 *)src;
         } else {
@@ -300,73 +288,42 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GroupTable tab)
     }
 }
 
-// ---------------------------------------------------------------------------
-// Skinny kernel for small M: one workgroup of 512 threads (8 waves) per
-// 64 x 256 output tile and K slice.  Wave w owns output columns
-// [64 (w%4), +64) over half of every K tile (64-K groups 2 (w/4) and
-// 2 (w/4) + 1); the two K halves are added through LDS at the end.  A 64 x 64
-// wave tile reads each A fragment from LDS once for two B column blocks: LDS
-// bandwidth (about 180 B/clk/CU measured), not MFMA, bounds a 64 x 32 tile.
-//
-// Memory side.  Every K tile (256 elements) the workgroup needs 256 B rows x
-// 128 packed bytes, their 16 scale bytes, and 64 A rows x 128 bytes.  Each
-// load instruction reads whole 128-byte lines (a wave covers 8 rows x 8 x 16
-// bytes), kDepth K tiles ahead, into registers; one step before use the
-// registers go to a double-buffered LDS stage: B and its scales as they are
-// (rows padded to 144 bytes so both the row-wise writes and the MFMA-layout
-// reads are bank-conflict free), A decoded to fp16 (each A element decoded
-// once per workgroup).
-//
-// Math side.  A wave reads, per 64-K group and B column block, 16 bytes of the
-// lane's B row for its half of the group, decodes 8 elements per 16 K
-// (v_cvt_scalef32_pk_f16_fp4 then v_pk_mul_f16 by the block scale) and runs
-// four 32x32x16 MFMAs: A rows 0-31 and 32-63 against its two column blocks.
-//
-// The K loop is a software pipeline, one step per K tile: compute tile t from
-// LDS stage t&1, refill register slot X with tile t + kDepth, move slot Y
-// (tile t + 1) into stage (t+1)&1, barrier.  sched_barrier fences stop the
-// compiler from hoisting the refill above the code that still reads the slot,
-// so it counts outstanding loads exactly instead of draining them.
-//
-// With split_k > 1 the K tiles are divided among split_k workgroups per output
-// tile and each writes its fp32 accumulators, in their MFMA register layout,
-// to the workspace; reduce_partials_kernel adds them in slice order.
-// ---------------------------------------------------------------------------
-namespace skinny {
-constexpr int BM = 64, BN = 256, BK = 256;
-constexpr int kThreads = 512;
-#ifndef NVFP4_SKINNY_DEPTH
-#define NVFP4_SKINNY_DEPTH 2
-#endif
-constexpr int kDepth = NVFP4_SKINNY_DEPTH; // K tiles in flight per thread
-constexpr int kA16Stride = BK * 2 + 16;    // bytes per decoded A row (padded)
-constexpr int kBStride = BK / 2 + 16;      // bytes per packed B row (padded)
-constexpr int kA16Bytes = BM * kA16Stride;
-constexpr int kBBytes = BN * kBStride;
-constexpr int kSfbBytes = BN * (BK / 16);
-constexpr int kStageBytes = kA16Bytes + kBBytes + kSfbBytes;
-constexpr int kTileElems = BM * BN;        // partial-sum floats per tile
-static_assert(2 * kStageBytes <= 160 * 1024, "two stages must fit in LDS");
-} // namespace skinny
-
-struct SkinnySlot {
-    u32x4 b[4];    // B chunks j = 0..3: row 64j + tid/8, bytes [16 (tid%8), +16)
-    u32x4 sfb;     // threads 0..255: the 16 scale bytes of B row tid
-    u32x4 a;       // A: row tid/8, 32 elements at K [32 (tid%8), +32)
-    uint32_t sfa;  // their two scale bytes
-};
-
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// kVec: K % 256 == 0 and SFB 16-byte aligned, so a row's 16 scale bytes of a
-// K tile are one aligned load.  Otherwise they are 8 two-byte loads (K % 32
-// == 0 makes each pair of blocks wholly inside or wholly past K) whose bytes
-// past K read as zero.
+namespace stream {
+constexpr int BM = 64, BN = 32, BK = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kRowBytes = BK / 2;            // packed bytes per row per K tile
+constexpr int kStride = kRowBytes + 16;      // padded LDS row
+constexpr int kSfBytes = BK / 16;            // scale bytes per row per K tile
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + BM * kStride;
+constexpr int kSfaOff = kBOff + BN * kStride;
+constexpr int kSfbOff = kSfaOff + BM * kSfBytes;
+constexpr int kWaveBytes = kSfbOff + BN * kSfBytes; // 14848
+constexpr int kTileElems = BM * BN;          // partial-sum floats per tile
+static_assert(kWaves * kWaveBytes <= 160 * 1024, "wave regions must fit in LDS");
+static_assert(kWaves * kTileElems * 4 <= kWaves * kWaveBytes, "reduction reuses the regions");
+} // namespace stream
+
+// One K tile of one wave, in registers: A 64 x 128 bytes as 8 lines of 8 rows,
+// B 32 x 128 bytes as 4, and the scales of row lane (A) / lane % 32 (B).
+struct StreamSlot {
+    u32x4 a[8];
+    u32x4 b[4];
+    u32x4 sfa;
+    u32x4 sfb;
+};
+
+// kVec: K % 256 == 0 and both scale arrays 16-byte aligned: a row's 16 scale
+// bytes of a K tile are one aligned load.  Otherwise they are 8 two-byte
+// loads (K % 32 == 0 makes each pair of blocks wholly inside or past K).
 template <bool kVec>
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(GroupTable tab, float *partials)
+__global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float *partials)
 {
-    using namespace skinny;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    using namespace stream;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kWaveBytes];
 
     const int S = tab.split_k;
     const int tile = blockIdx.x / S;
@@ -387,224 +344,172 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GroupTable tab, float 
 
     const int kb_row = K / 2;
     const int ks_row = K / 16;
+    // this workgroup's K tiles, then this wave's share of them
     const int nkt = (K + BK - 1) / BK;
-    const int kt0 = (int)((long)split * nkt / S);
-    const int kt1 = (int)((long)(split + 1) * nkt / S);
+    const int s0 = (int)((long)split * nkt / S), s1 = (int)((long)(split + 1) * nkt / S);
+    const int kt0 = s0 + (s1 - s0) * wave / kWaves;
+    const int kt1 = s0 + (s1 - s0) * (wave + 1) / kWaves;
 
-    // this workgroup's B rows [col0, col0 + 256); rows past N read as zero
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
+    // rows past M / N read as zero (beyond num_records)
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
 
-    // loop-invariant per-thread offsets
-    const int crow = tid >> 3, c16 = tid & 7; // chunk row (within 64) and 16-byte column
-    uint32_t boff[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        boff[j] = (uint32_t)((64 * j + crow) * kb_row + c16 * 16);
-    const uint32_t sboff = (uint32_t)((tid & 255) * ks_row);
-    const uint32_t aoff = (uint32_t)(crow * kb_row + c16 * 16);
-    const uint32_t saoff = (uint32_t)(crow * ks_row + c16 * 2);
-    const bool sfb_loader = wave < 4; // waves 0-3 carry the B scales
+    // loop-invariant offsets: line loads cover rows 8j + lane/8, bytes 16 (lane%8)
+    const int lrow = lane >> 3, c16 = lane & 7;
+    const uint32_t line_off = (uint32_t)(lrow * kb_row + c16 * 16);
+    const uint32_t sfa_off = (uint32_t)(lane * ks_row);
+    const uint32_t sfb_off = (uint32_t)(l32 * ks_row);
 
-    auto load = [&](SkinnySlot &s, int kt) {
+    auto load = [&](StreamSlot &s, int kt) {
         const bool live = kt < kt1;
-        const uint32_t kb = (uint32_t)kt * (BK / 2), ks = (uint32_t)kt * (BK / 16);
-        // a 16-byte chunk at column c16 holds K [kt*256 + 32 c16, +32): wholly
-        // inside or wholly past K
-        const bool cin = live && (int)(kb + c16 * 16) < kb_row;
+        const int kb = kt * kRowBytes, ks = kt * kSfBytes;
+        const bool cin = live && (kb + c16 * 16) < kb_row; // chunk inside K
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rA, cin ? line_off + (uint32_t)(8 * j * kb_row + kb) : kOutOfRange, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, cin ? boff[j] + kb : kOutOfRange, 0, 0);
-        if (sfb_loader) {
-            if (kVec) {
-                s.sfb = __builtin_amdgcn_raw_buffer_load_b128(rSB, live ? sboff + ks : kOutOfRange, 0, 0);
-            } else {
+            s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rB, cin ? line_off + (uint32_t)(8 * j * kb_row + kb) : kOutOfRange, 0, 0);
+        if (kVec) {
+            s.sfa = __builtin_amdgcn_raw_buffer_load_b128(rSA, live ? sfa_off + ks : kOutOfRange, 0, 0);
+            s.sfb = __builtin_amdgcn_raw_buffer_load_b128(rSB, live ? sfb_off + ks : kOutOfRange, 0, 0);
+        } else {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const bool ok0 = live && (int)(ks + 4 * p) < ks_row;
-                    const bool ok1 = live && (int)(ks + 4 * p + 2) < ks_row;
-                    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rSB, ok0 ? sboff + ks + 4 * p : kOutOfRange, 0, 0);
-                    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rSB, ok1 ? sboff + ks + 4 * p + 2 : kOutOfRange, 0, 0);
-                    s.sfb[p] = lo | (hi << 16);
-                }
+            for (int p = 0; p < 4; ++p) {
+                const bool ok0 = live && (ks + 4 * p) < ks_row;
+                const bool ok1 = live && (ks + 4 * p + 2) < ks_row;
+                const uint32_t a0 = __builtin_amdgcn_raw_buffer_load_b16(rSA, ok0 ? sfa_off + ks + 4 * p : kOutOfRange, 0, 0);
+                const uint32_t a1 = __builtin_amdgcn_raw_buffer_load_b16(rSA, ok1 ? sfa_off + ks + 4 * p + 2 : kOutOfRange, 0, 0);
+                const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b16(rSB, ok0 ? sfb_off + ks + 4 * p : kOutOfRange, 0, 0);
+                const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b16(rSB, ok1 ? sfb_off + ks + 4 * p + 2 : kOutOfRange, 0, 0);
+                s.sfa[p] = a0 | (a1 << 16);
+                s.sfb[p] = b0 | (b1 << 16);
             }
         }
-        s.a = __builtin_amdgcn_raw_buffer_load_b128(rA, cin ? aoff + kb : kOutOfRange, 0, 0);
-        s.sfa = __builtin_amdgcn_raw_buffer_load_b16(rSA, cin ? saoff + ks : kOutOfRange, 0, 0);
     };
 
-    // slot -> LDS stage, in two parts so they can sit between the two halves
-    // of the previous tile's MFMA work: A decoded to fp16, then packed B and
-    // its scales as they are
-    auto stage_a = [&](const SkinnySlot &s, int buf) {
-        uint8_t *st = lds + buf * kStageBytes;
-        const half2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s.sfa, 1.0f, false);
-        uint8_t *dst = st + crow * kA16Stride + c16 * 64;
-        *(half8_t *)(dst + 0) = decode8(s.a.x, bcast_lo(sc));
-        *(half8_t *)(dst + 16) = decode8(s.a.y, bcast_lo(sc));
-        *(half8_t *)(dst + 32) = decode8(s.a.z, bcast_hi(sc));
-        *(half8_t *)(dst + 48) = decode8(s.a.w, bcast_hi(sc));
-    };
-    auto stage_b = [&](const SkinnySlot &s, int buf) {
-        uint8_t *sb = lds + buf * kStageBytes + kA16Bytes;
+    uint8_t *wl = lds + wave * kWaveBytes; // this wave's region
+
+    auto put = [&](const StreamSlot &s) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *(u32x4 *)(wl + kAOff + (8 * j + lrow) * kStride + c16 * 16) = s.a[j];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *(u32x4 *)(sb + (64 * j + crow) * kBStride + c16 * 16) = s.b[j];
-        if (sfb_loader)
-            *(u32x4 *)(sb + kBBytes + tid * 16) = s.sfb;
+            *(u32x4 *)(wl + kBOff + (8 * j + lrow) * kStride + c16 * 16) = s.b[j];
+        *(u32x4 *)(wl + kSfaOff + lane * kSfBytes) = s.sfa;
+        if (h == 0)
+            *(u32x4 *)(wl + kSfbOff + l32 * kSfBytes) = s.sfb;
     };
 
-    const int nq = wave & 3;  // 64-column block of this wave
-    const int kh = wave >> 2; // K half of every K tile
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-            acc[a][b] = (f32x16){};
+    f32x16 acc0 = (f32x16){}, acc1 = (f32x16){};
     const uint32_t sh = h * 16;
 
-    // MFMA work of one 64-K group (ii = 0, 1 of this wave's K half)
-    auto compute = [&](int buf, int ii) {
-        const uint8_t *st = lds + buf * kStageBytes;
-        const uint8_t *arow0 = st + l32 * kA16Stride + h * 64;
-        const uint8_t *arow1 = arow0 + 32 * kA16Stride;
-        const uint8_t *bro[2];
-        u32x4 sfrow[2];
+    auto compute = [&]() {
+        const uint8_t *a0 = wl + kAOff + l32 * kStride + h * 16;
+        const uint8_t *a1 = a0 + 32 * kStride;
+        const uint8_t *b0 = wl + kBOff + l32 * kStride + h * 16;
+        const u32x4 sa0 = *(const u32x4 *)(wl + kSfaOff + l32 * kSfBytes);
+        const u32x4 sa1 = *(const u32x4 *)(wl + kSfaOff + (32 + l32) * kSfBytes);
+        const u32x4 sb = *(const u32x4 *)(wl + kSfbOff + l32 * kSfBytes);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int brow = nq * 64 + c * 32 + l32;
-            bro[c] = st + kA16Bytes + brow * kBStride + h * 16;
-            sfrow[c] = *(const u32x4 *)(st + kA16Bytes + kBBytes + brow * 16);
-        }
-        {
-            const int i = 2 * kh + ii; // 64-K group
-            // issue every LDS read of the group before the first MFMA
-            u32x4 bq[2];
-            half8_t fa[4][2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                bq[c] = *(const u32x4 *)(bro[c] + i * 32);
+        for (int i = 0; i < 4; ++i) {
+            // this lane's half of 64-K group i: chunk 2i + h, blocks 4i+2h, 4i+2h+1
+            const u32x4 pa0 = *(const u32x4 *)(a0 + i * 32);
+            const u32x4 pa1 = *(const u32x4 *)(a1 + i * 32);
+            const u32x4 pb = *(const u32x4 *)(b0 + i * 32);
+            const half2_t ca0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa0[i] >> sh, 1.0f, false);
+            const half2_t ca1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa1[i] >> sh, 1.0f, false);
+            const half2_t cb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[i] >> sh, 1.0f, false);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                fa[q][0] = *(const half8_t *)(arow0 + i * 128 + q * 16);
-                fa[q][1] = *(const half8_t *)(arow1 + i * 128 + q * 16);
-            }
-            half2_t sb[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-                // scales of this lane's half in group i: blocks 4i+2h, 4i+2h+1
-                sb[c] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sfrow[c][i] >> sh, 1.0f, false);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const half8_t fb = decode8(bq[c][q], q < 2 ? bcast_lo(sb[c]) : bcast_hi(sb[c]));
-                    acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[q][0], fb, acc[0][c], 0, 0, 0);
-                    acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[q][1], fb, acc[1][c], 0, 0, 0);
-                }
+                const half8_t fa0 = decode8(pa0[q], q < 2 ? bcast_lo(ca0) : bcast_hi(ca0));
+                const half8_t fa1 = decode8(pa1[q], q < 2 ? bcast_lo(ca1) : bcast_hi(ca1));
+                const half8_t fb = decode8(pb[q], q < 2 ? bcast_lo(cb) : bcast_hi(cb));
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa0, fb, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa1, fb, acc1, 0, 0, 0);
             }
         }
     };
 
-    // one pipeline step: refill slot X (staged into LDS last step) with tile
-    // t + kDepth, run tile t's MFMA work from stage t&1 with slot Y (tile
-    // t + 1) moved into stage (t+1)&1 between its two halves, barrier.  Steps
-    // past the slice's last tile only keep the pipeline's shape: no MFMA
-    // work, and their loads read zeros.
-    auto step = [&](int t, SkinnySlot &X, SkinnySlot &Y) {
-        load(X, t + kDepth);
+    // step: move slot X (tile t) into LDS, refill it with tile t + 2, compute
+    auto step = [&](int t, StreamSlot &X) {
+        put(X);
         SCHED_FENCE();
-        const bool live = t < kt1;
-        if (live)
-            compute(t & 1, 0);
-        stage_a(Y, (t + 1) & 1);
-        if (live)
-            compute(t & 1, 1);
-        stage_b(Y, (t + 1) & 1);
-        __syncthreads();
+        load(X, t + 2);
+        SCHED_FENCE();
+        if (t < kt1)
+            compute();
         SCHED_FENCE();
     };
 
     if (kt1 > kt0) {
-        SkinnySlot sl[kDepth]; // indexed by constants only: stays in registers
-#pragma unroll
-        for (int j = 0; j < kDepth; ++j) {
-            load(sl[j], kt0 + j);
-            SCHED_FENCE();
-        }
-        stage_a(sl[0], kt0 & 1);
-        stage_b(sl[0], kt0 & 1);
-        __syncthreads();
+        StreamSlot x0, x1;
+        load(x0, kt0);
         SCHED_FENCE();
-        // slot 0 is in LDS: the first step refills it
-        for (int t = kt0; t < kt1; t += kDepth) {
-#pragma unroll
-            for (int j = 0; j < kDepth; ++j)
-                step(t + j, sl[j], sl[(j + 1) % kDepth]);
+        load(x1, kt0 + 1);
+        SCHED_FENCE();
+        for (int t = kt0; t < kt1; t += 2) {
+            step(t, x0);
+            step(t + 1, x1);
         }
     }
 
-    // add the two K halves: waves 4-7 hand their sums to waves 0-3 via LDS
-    // (the stages are free: the loop ended with a barrier)
-    float *red = (float *)lds + nq * (4 * 16 * 64) + lane;
-    if (kh == 1) {
+    // add the eight waves' partial sums through LDS (row-major 64 x 32 each)
+    __syncthreads();
+    float *red = (float *)lds;
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    red[((a * 2 + b) * 16 + e) * 64] = acc[a][b][e];
+    for (int e = 0; e < 16; ++e) {
+        const int rr = (e >> 2) * 8 + h * 4 + (e & 3);
+        red[wave * kTileElems + rr * BN + l32] = acc0[e];
+        red[wave * kTileElems + (32 + rr) * BN + l32] = acc1[e];
     }
     __syncthreads();
-    if (kh == 1)
-        return;
+    const int e0 = tid * 4; // 4 consecutive columns of one row
+    float4 sum = *(const float4 *)(red + e0);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[a][b][e] += red[((a * 2 + b) * 16 + e) * 64];
-
+    for (int w = 1; w < kWaves; ++w) {
+        const float4 v = *(const float4 *)(red + w * kTileElems + e0);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
     if (S > 1) {
-        // partial tile in register layout: [nq][rb][cb][reg][lane]
-        float *dst = partials + ((long)tile * S + split) * kTileElems + nq * (4 * 16 * 64) + lane;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    dst[((a * 2 + b) * 16 + e) * 64] = acc[a][b][e];
+        *(float4 *)(partials + ((long)tile * S + split) * kTileElems + e0) = sum;
         return;
     }
-    // single slice: round to fp16 and store straight from the accumulators
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int gcol = col0 + nq * 64 + b * 32 + l32;
-        if (gcol >= N)
-            continue;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int grow = row0 + a * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-                if (grow < M)
-                    d.C[(long)grow * N + gcol] = __builtin_bit_cast(uint16_t, (_Float16)acc[a][b][e]);
-            }
+    const int row = row0 + e0 / BN, col = col0 + e0 % BN;
+    if (row >= M)
+        return;
+    uint16_t *dst = d.C + (long)row * N + col;
+    const uint16_t v0 = __builtin_bit_cast(uint16_t, (_Float16)sum.x);
+    const uint16_t v1 = __builtin_bit_cast(uint16_t, (_Float16)sum.y);
+    const uint16_t v2 = __builtin_bit_cast(uint16_t, (_Float16)sum.z);
+    const uint16_t v3 = __builtin_bit_cast(uint16_t, (_Float16)sum.w);
+    if (col + 4 <= N && (((uintptr_t)dst) & 7) == 0) {
+        *(u32x2 *)dst = (u32x2){(uint32_t)v0 | ((uint32_t)v1 << 16), (uint32_t)v2 | ((uint32_t)v3 << 16)};
+    } else {
+        if (col < N)
+            dst[0] = v0;
+        if (col + 1 < N)
+            dst[1] = v1;
+        if (col + 2 < N)
+            dst[2] = v2;
+        if (col + 3 < N)
+            dst[3] = v3;
     }
 }
 
-// Sums the split_k partial tiles of the skinny kernel in slice order and
-// writes fp16 C.  Thread -> 4 consecutive floats of one tile's partial, which
-// in the MFMA register layout are 4 adjacent columns of one output row.
+// Sums the split_k row-major partial tiles (64 x 32 fp32 each) of one output
+// tile in slice order and writes fp16 C.  Thread -> 4 consecutive columns.
 __global__ __launch_bounds__(256) void reduce_partials_kernel(GroupTable tab, const float *partials)
 {
-    using namespace skinny;
+    using namespace stream;
     const long e = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
     const int tile = (int)(e / kTileElems);
     const int idx = (int)(e - (long)tile * kTileElems);
@@ -625,14 +530,8 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(GroupTable tab, co
         acc.z += v.z;
         acc.w += v.w;
     }
-    // register layout [nq][rb][cb][reg][lane] of the skinny kernel's partials
-    const int lane0 = idx & 63;
-    const int reg = (idx >> 6) & 15;
-    const int cb = (idx >> 10) & 1;
-    const int rb = (idx >> 11) & 1;
-    const int nq = idx >> 12;
-    const int row = tm * BM + rb * 32 + (reg >> 2) * 8 + (lane0 >> 5) * 4 + (reg & 3);
-    const int col = tn * BN + nq * 64 + cb * 32 + (lane0 & 31);
+    const int row = tm * BM + idx / BN;
+    const int col = tn * BN + idx % BN;
     if (row >= d.M)
         return;
     uint16_t *dst = d.C + (long)row * d.N + col;
@@ -664,17 +563,18 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
     if (total <= 0)
         return hipSuccess;
     switch (cfg) {
-    case kSkinny64x256: {
+    case kStream64x32: {
         float *partials = (float *)workspace;
         void *args[] = {const_cast<GroupTable *>(&table), &partials};
         bool vec = true;
         for (int g = 0; g < table.num_groups; ++g)
-            vec = vec && (table.g[g].K % skinny::BK) == 0 && (((uintptr_t)table.g[g].SFB) & 15) == 0;
-        const void *fn = vec ? (const void *)gemm_skinny_kernel<true> : (const void *)gemm_skinny_kernel<false>;
-        hipError_t e = hipLaunchKernel(fn, dim3(total), dim3(skinny::kThreads), args, 0, stream);
+            vec = vec && (table.g[g].K % stream::BK) == 0 &&
+                  ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
+        const void *fn = vec ? (const void *)gemm_stream_kernel<true> : (const void *)gemm_stream_kernel<false>;
+        hipError_t e = hipLaunchKernel(fn, dim3(total), dim3(stream::kThreads), args, 0, stream);
         if (e != hipSuccess || table.split_k == 1)
             return e;
-        const long threads = (long)tiles * skinny::kTileElems / 4;
+        const long threads = (long)tiles * stream::kTileElems / 4;
         const float *cpart = partials;
         void *rargs[] = {const_cast<GroupTable *>(&table), &cpart};
         return hipLaunchKernel((const void *)reduce_partials_kernel, dim3((unsigned)((threads + 255) / 256)),
@@ -683,8 +583,12 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
     case kTile128x128:
     default: {
         void *args[] = {const_cast<GroupTable *>(&table)};
-        return hipLaunchKernel((const void *)gemm_tiled_kernel<128, 128, 128>, dim3(total),
-                               dim3(256), args, 0, stream);
+        bool vec = true;
+        for (int g = 0; g < table.num_groups; ++g)
+            vec = vec && (table.g[g].K % tiled::BK) == 0 &&
+                  ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 7) == 0;
+        const void *fn = vec ? (const void *)gemm_tiled_kernel<true> : (const void *)gemm_tiled_kernel<false>;
+        return hipLaunchKernel(fn, dim3(total), dim3(64), args, 0, stream);
     }
     }
 }

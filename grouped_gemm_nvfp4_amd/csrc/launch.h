@@ -36,8 +36,8 @@ struct GroupTable {
 
 // Tile configurations the kernels are built for.
 enum TileConfig : int {
-    kTile128x128 = 0, // 4 waves, 2x2 of 64x64 wave tiles
-    kSkinny64x256 = 1, // 8 waves side by side in N; A decoded once into LDS; K may be split
+    kTile128x128 = 0, // one wave per workgroup owning the whole 128 x 128 tile
+    kStream64x32 = 1,  // 8 waves split K; each streams its own share; K may be split
 };
 
 struct TileShape {
@@ -47,8 +47,8 @@ struct TileShape {
 inline TileShape tile_shape(TileConfig c)
 {
     switch (c) {
-    case kSkinny64x256:
-        return {64, 256, 128};
+    case kStream64x32:
+        return {64, 32, 256};
     case kTile128x128:
     default:
         return {128, 128, 128};

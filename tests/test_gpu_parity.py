@@ -101,10 +101,10 @@ def test_edge_shapes(lib, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [
     (64, 7168, 2080), (40, 1000, 1536), (64, 300, 16384), (1, 4097, 4096),
-    (63, 257, 96), (33, 513, 8192),
+    (63, 257, 96), (33, 513, 8192), (64, 64, 16384), (5, 40, 9984),
 ])
 def test_small_m_split_k_shapes(lib, M, N, K):
-    """M <= 64 takes the skinny kernel; few tiles make it split K."""
+    """M <= 64 takes the stream kernel; few tiles make it split K as well."""
     info = lib.gemm_plan(M, N, K)
     assert info["tile_m"] == 64
     p = inputs.draw_problems(3000 + M + N + K, [(M, N, K)])[0]
@@ -207,8 +207,8 @@ def test_group_small_full_compare(lib):
 
 def test_group_small_m_split_k(lib):
     rng = np.random.default_rng(36)
-    shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 700)), 32 * int(rng.integers(1, 40)))
-              for _ in range(12)] + [(0, 64, 64), (64, 64, 0)]
+    shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 200)), 32 * int(rng.integers(64, 160)))
+              for _ in range(4)] + [(0, 64, 64), (64, 64, 0), (7, 33, 96)]
     info, _ = lib.group_gemm_plan(shapes)
     assert info["split_k"] > 1
     probs = inputs.draw_problems(37, shapes)
