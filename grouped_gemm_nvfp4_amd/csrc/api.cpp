@@ -10,7 +10,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <map>
+#include <numeric>
+#include <queue>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -55,9 +58,34 @@ struct Plan {
     TileConfig cfg;
     int tile_m, tile_n, split_k;
     std::vector<int> prefix; // per input group, num_groups + 1 entries
+    std::vector<int> order;  // launch order of the groups (longest K first)
     long long total_tiles;
     long long workspace_bytes;
 };
+
+// Workgroup slots of an MI355X: 256 CUs x 4 SIMDs for one-wave workgroups.
+constexpr int kWaveSlots = 1024;
+
+// Makespan, in K tiles, of list-scheduling `per_tile` work items (in launch
+// order) onto `slots` identical slots, as the hardware dispatcher does when
+// each new workgroup takes the first free slot.
+long long list_makespan(const std::vector<std::pair<long long, long long>> &groups, int slots)
+{
+    // groups: (tile count, K tiles per tile), in launch order
+    std::priority_queue<long long, std::vector<long long>, std::greater<long long>> q;
+    for (int i = 0; i < slots; ++i)
+        q.push(0);
+    long long end = 0;
+    for (const auto &g : groups)
+        for (long long t = 0; t < g.first; ++t) {
+            long long s = q.top();
+            q.pop();
+            s += g.second;
+            end = std::max(end, s);
+            q.push(s);
+        }
+    return end;
+}
 
 // Workspaces for K-split launches, one per (device, stream): work on one
 // stream runs in order, so a stream's calls never use its workspace
@@ -156,6 +184,36 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         plan->prefix[g + 1] = (int)total;
     }
     plan->total_tiles = total;
+    // Launch order: longest K first, so in-order dispatch is longest-first
+    // (groups of equal K keep their order).
+    plan->order.resize(num_groups);
+    std::iota(plan->order.begin(), plan->order.end(), 0);
+    std::stable_sort(plan->order.begin(), plan->order.end(), [&](int a, int b) {
+        return problems[a].K > problems[b].K;
+    });
+    if (plan->cfg == nvfp4::kTile128x128 && total > 0 && total < 4 * kWaveSlots) {
+        // Few tiles: compare one wave per tile (kWaveSlots slots) with four
+        // waves splitting each tile's K (kWaveSlots / 4 slots, a quarter of the
+        // K tiles each, plus about 3% for adding the sums).
+        std::vector<std::pair<long long, long long>> g1, g4;
+        for (int gi : plan->order) {
+            const nvfp4_problem &p = problems[gi];
+            const long long t = plan->prefix[gi + 1] - plan->prefix[gi];
+            if (t == 0)
+                continue;
+            const long long kt = std::max(1, (p.K + ts.tile_k - 1) / ts.tile_k);
+            g1.emplace_back(t, 4 * kt);
+            g4.emplace_back(t, kt + 1);
+        }
+        // Measured: per K tile the four-wave form is slower than four
+        // independent one-wave workgroups (the 8-group and 2-group workloads
+        // ran 10-17% slower with it), so it is taken only where the model
+        // promises at least a factor of two: few, long tiles.
+        const long long m1 = list_makespan(g1, kWaveSlots);
+        const long long m4 = list_makespan(g4, kWaveSlots / 4) * 103 / 100;
+        if (2 * m4 < m1)
+            plan->cfg = nvfp4::kTile128x128K4;
+    }
     // Split K only where the kernel supports it and the tiles alone leave
     // compute units idle: at most kTargetWorkgroups workgroups in all, so each
     // runs once, in a single wave of workgroups.
@@ -169,7 +227,9 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
 
 void fill_info(const Plan &plan, nvfp4_plan_info *info)
 {
-    info->kernel = plan.total_tiles > 0 ? (plan.split_k > 1 ? 2 : 1) : 0;
+    info->kernel = plan.total_tiles == 0 ? 0
+                   : plan.split_k > 1 ? 2
+                   : plan.cfg == nvfp4::kTile128x128K4 ? 3 : 1;
     info->tile_m = plan.tile_m;
     info->tile_n = plan.tile_n;
     info->split_k = plan.split_k;
@@ -204,7 +264,7 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
         table.prefix[0] = 0;
         return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
     };
-    for (int g = 0; g < num_groups; ++g) {
+    for (int g : plan.order) {
         const nvfp4_problem &p = problems[g];
         const int tiles = plan.prefix[g + 1] - plan.prefix[g];
         if (tiles == 0)

@@ -122,11 +122,15 @@ struct TiledSlot {
 
 // kVec: K % 128 == 0 and both scale arrays 8-byte aligned (one 8-byte load
 // per row and K tile); otherwise 2-byte loads, pairs past K read as zero.
-template <bool kVec>
-__global__ __launch_bounds__(64) void gemm_tiled_kernel(GroupTable tab)
+// kWaves (1 or 4): waves per workgroup.  With 4, the waves split the tile's K
+// tiles four ways (one per SIMD of the CU, each with its own LDS stages) and
+// their sums are added through LDS at the end: used when tiles alone would
+// leave SIMDs idle.
+template <bool kVec, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void gemm_tiled_kernel(GroupTable tab)
 {
     using namespace tiled;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_all[kWaves * 2 * kStageBytes];
 
     const int w = blockIdx.x;
     const int gi = find_group(tab, w);
@@ -137,13 +141,18 @@ __global__ __launch_bounds__(64) void gemm_tiled_kernel(GroupTable tab)
     const int M = d.M, N = d.N, K = d.K;
     const int row0 = tm * BM, col0 = tn * BN;
 
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = kWaves == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5;
     const int l32 = lane & 31;
+    uint8_t *lds = lds_all + wave * 2 * kStageBytes; // this wave's stages
 
     const int kb_row = K / 2;
     const int ks_row = K / 16;
-    const int nkt = (K + BK - 1) / BK;
+    const int nkt_all = (K + BK - 1) / BK;
+    // this wave's K tiles [kt_base, kt_base + nkt)
+    const int kt_base = (int)((long)nkt_all * wave / kWaves);
+    const int nkt = (int)((long)nkt_all * (wave + 1) / kWaves) - kt_base;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(64) void gemm_tiled_kernel(GroupTable tab)
 
     auto load = [&](TiledSlot &s, int kt) {
         const bool live = kt < nkt;
-        const int kb = kt * kRowBytes, ks = kt * kSfBytes;
+        const int kb = (kt_base + kt) * kRowBytes, ks = (kt_base + kt) * kSfBytes;
         const bool cin = live && (kb + c16 * 16) < kb_row; // chunk inside K
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -253,24 +262,61 @@ __global__ __launch_bounds__(64) void gemm_tiled_kernel(GroupTable tab)
         }
     }
 
-    // epilogue: fp32 -> fp16 (round to nearest even) into LDS, then 16-byte
-    // row-contiguous stores masked to M x N.  The stages are free: the wave's
-    // own LDS accesses are ordered.
-    uint8_t *sC = lds;
+    if (kWaves > 1) {
+        // add the waves' sums: 3 -> 1 and 2 -> 0, then 1 -> 0, through LDS in
+        // register order ([reg][lane]: full 256-byte rows, conflict free)
+        float *red = (float *)lds_all;
+        constexpr int kAccFloats = 4 * 4 * 16 * 64;
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int round = 0; round < 2; ++round) {
+            const int give_lo = round == 0 ? 2 : 1; // waves [give_lo, 2 give_lo) hand over
+            if (wave >= give_lo && wave < 2 * give_lo) {
+                float *dst = red + (wave - give_lo) * kAccFloats + lane;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
-                const int col = 32 * j + l32;
-                *(uint16_t *)(sC + row * kCStride + col * 2) = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            dst[((i * 4 + j) * 16 + e) * 64] = acc[i][j][e];
             }
+            __syncthreads();
+            if (wave < give_lo) {
+                const float *src = red + wave * kAccFloats + lane;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[i][j][e] += src[((i * 4 + j) * 16 + e) * 64];
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue: fp32 -> fp16 (round to nearest even) into LDS by wave 0, then
+    // 16-byte row-contiguous stores masked to M x N by all waves.
+    uint8_t *sC = lds_all;
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
+                    const int col = 32 * j + l32;
+                    *(uint16_t *)(sC + row * kCStride + col * 2) = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
+                }
+    }
+    if (kWaves > 1)
+        __syncthreads();
     const bool vec_ok = (N % 8 == 0) && ((((uintptr_t)d.C) & 15) == 0);
 #pragma unroll 4
-    for (int s = 0; s < BM * BN / 8 / 64; ++s) {
-        const int seg = s * 64 + lane;
+    for (int s = 0; s < BM * BN / 8 / (64 * kWaves); ++s) {
+        const int seg = s * 64 * kWaves + (int)threadIdx.x;
         const int row = seg >> 4, c8 = (seg & 15) * 8;
         const int grow = row0 + row, gcol = col0 + c8;
         if (grow >= M)
@@ -580,6 +626,7 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         return hipLaunchKernel((const void *)reduce_partials_kernel, dim3((unsigned)((threads + 255) / 256)),
                                dim3(256), rargs, 0, stream);
     }
+    case kTile128x128K4:
     case kTile128x128:
     default: {
         void *args[] = {const_cast<GroupTable *>(&table)};
@@ -587,8 +634,10 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % tiled::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 7) == 0;
-        const void *fn = vec ? (const void *)gemm_tiled_kernel<true> : (const void *)gemm_tiled_kernel<false>;
-        return hipLaunchKernel(fn, dim3(total), dim3(64), args, 0, stream);
+        const bool four = cfg == kTile128x128K4;
+        const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
+                              : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);
+        return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
     }
     }
 }

@@ -36,8 +36,9 @@ struct GroupTable {
 
 // Tile configurations the kernels are built for.
 enum TileConfig : int {
-    kTile128x128 = 0, // one wave per workgroup owning the whole 128 x 128 tile
-    kStream64x32 = 1,  // 8 waves split K; each streams its own share; K may be split
+    kTile128x128 = 0,   // one wave per workgroup owning the whole 128 x 128 tile
+    kStream64x32 = 1,   // 8 waves split K; each streams its own share; K may be split
+    kTile128x128K4 = 2, // 128 x 128 tile, four waves splitting its K, sums added in LDS
 };
 
 struct TileShape {
@@ -49,6 +50,7 @@ inline TileShape tile_shape(TileConfig c)
     switch (c) {
     case kStream64x32:
         return {64, 32, 256};
+    case kTile128x128K4:
     case kTile128x128:
     default:
         return {128, 128, 128};

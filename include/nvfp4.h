@@ -99,7 +99,8 @@ nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups,
 /* How a call would be carried out (host only, no HIP call).  For tests and
  * reports. */
 typedef struct {
-    int kernel;      /* 0: nothing to launch, 1: tiled kernel, 2: K-split kernel */
+    int kernel;      /* 0: nothing to launch, 1: one tile per workgroup, 2: K split
+                        across workgroups, 3: K split across a workgroup's waves */
     int tile_m;      /* output rows per workgroup */
     int tile_n;      /* output columns per workgroup */
     int split_k;     /* K slices per output tile (1 = none) */

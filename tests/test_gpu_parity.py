@@ -111,6 +111,21 @@ def test_small_m_split_k_shapes(lib, M, N, K):
     check_full(lib, p, "small-M %dx%dx%d split %d" % (M, N, K, info["split_k"]))
 
 
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (1024, 65536, 128, 1),   # >= 4096 tiles: one wave per 128x128 tile
+    (1000, 520, 1184, 3),    # few tiles: four waves split each tile's K
+])
+def test_tiled_variants(lib, M, N, K, kernel):
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == kernel and info["tile_m"] == 128
+    p = inputs.draw_problems(4000 + M + K, [(M, N, K)])[0]
+    if M * N <= 1 << 20:
+        check_full(lib, p, "tiled %dx%dx%d" % (M, N, K))
+    else:
+        got = run_gemm(lib, p)
+        check_sampled(got, p, 91, "tiled %dx%dx%d" % (M, N, K))
+
+
 def test_all_ones_gives_exactly_K(lib):
     M, N, K = 130, 70, 7168
     ones = inputs.Problem(M, N, K, np.full((M, K // 2), 0x22, np.uint8),
