@@ -128,6 +128,11 @@ nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
     void *p = nullptr;
     if (hipMalloc(&p, rounded) != hipSuccess)
         return NVFP4_ERROR_LAUNCH;
+    // the tile counters start at zero (stream order puts this before any use)
+    if (hipMemsetAsync(p, 0, (size_t)nvfp4::kCounterBytes, stream) != hipSuccess) {
+        (void)hipFree(p);
+        return NVFP4_ERROR_LAUNCH;
+    }
     if (e.first != nullptr)
         w.retired.emplace_back(dev, e.first);
     e = std::make_pair(p, rounded);
@@ -135,21 +140,52 @@ nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
     return NVFP4_OK;
 }
 
-// Stream tiles (64 x 32, eight waves splitting K; K also split across
-// workgroups when the tiles alone cannot fill the chip) when every group has
-// M <= 64; 128 x 128 otherwise.
-TileConfig choose_config(const nvfp4_problem *problems, int num_groups)
-{
-    int max_m = 0;
-    for (int g = 0; g < num_groups; ++g)
-        if (!empty_output(problems[g]))
-            max_m = std::max(max_m, problems[g].M);
-    return (max_m > 0 && max_m <= 64) ? nvfp4::kStream64x32 : nvfp4::kTile128x128;
-}
-
 // Workgroups that keep every compute unit of an MI355X busy.
 constexpr int kTargetWorkgroups = 256;
+// K is split only when total * 2 <= kTargetWorkgroups: within the counters
+static_assert(kTargetWorkgroups / 2 <= nvfp4::kMaxSplitTiles, "split launches fit the tile counters");
 constexpr int kMaxSplitK = 16;
+// The 64 x 64 panel kernel is taken for M <= 64 when its launch fills at
+// least this many compute units; below that the 64 x 32 stream kernel, with
+// twice the tiles, keeps more of the chip busy (measured: it is faster on
+// 64x2048x7168, 32x4096x4096, 64x1024x16384, 64x7168x2080; the panel kernel
+// on 64x7168x16384, 1x7168x16384, 64x16384x4096).
+constexpr int kPanelMinWorkgroups = 192;
+
+// Output tiles of every group under tile shape ts (prefix[g + 1] is the
+// running total) and the longest K in K tiles.
+nvfp4_status count_tiles(const nvfp4_problem *problems, int num_groups, const nvfp4::TileShape &ts,
+                         std::vector<int> *prefix, long long *total, int *max_ktiles)
+{
+    prefix->assign(num_groups + 1, 0);
+    *total = 0;
+    *max_ktiles = 0;
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        long long t = 0;
+        if (!empty_output(p)) {
+            t = (long long)((p.M + ts.tile_m - 1) / ts.tile_m) * (long long)((p.N + ts.tile_n - 1) / ts.tile_n);
+            *max_ktiles = std::max(*max_ktiles, (p.K + ts.tile_k - 1) / ts.tile_k);
+        }
+        *total += t;
+        if (*total > kMaxWorkgroups)
+            return NVFP4_ERROR_NOT_SUPPORTED;
+        (*prefix)[g + 1] = (int)*total;
+    }
+    return NVFP4_OK;
+}
+
+// K slices per tile for the small-M kernels: split only where the tiles alone
+// leave compute units idle, to at most kTargetWorkgroups workgroups in all (so
+// each runs once, in a single wave of workgroups), keeping at least
+// min_ktiles K tiles per slice.
+int small_m_split(long long total, int max_ktiles, int min_ktiles)
+{
+    if (total <= 0 || total * 2 > kTargetWorkgroups)
+        return 1;
+    return (int)std::min<long long>(
+        {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles / min_ktiles), (long long)kMaxSplitK});
+}
 
 nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan)
 {
@@ -162,27 +198,39 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         if (s != NVFP4_OK)
             return s;
     }
-    plan->cfg = choose_config(problems, num_groups);
+    int max_m = 0;
+    for (int g = 0; g < num_groups; ++g)
+        if (!empty_output(problems[g]))
+            max_m = std::max(max_m, problems[g].M);
+
+    long long total = 0;
+    int max_ktiles = 0;
+    nvfp4_status s = NVFP4_OK;
+    plan->split_k = 1;
+    if (max_m > 0 && max_m <= 64) {
+        // panel: each wave takes at least one 256-K tile of a slice (8 waves)
+        plan->cfg = nvfp4::kPanel64x64;
+        s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
+        if (s != NVFP4_OK)
+            return s;
+        plan->split_k = small_m_split(total, max_ktiles, 8);
+        if (total * plan->split_k < kPanelMinWorkgroups) {
+            // stream: a slice keeps at least 4 K tiles, half a tile per wave
+            plan->cfg = nvfp4::kStream64x32;
+            s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
+            if (s != NVFP4_OK)
+                return s;
+            plan->split_k = small_m_split(total, max_ktiles, 4);
+        }
+    } else {
+        plan->cfg = nvfp4::kTile128x128;
+        s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
+        if (s != NVFP4_OK)
+            return s;
+    }
     const nvfp4::TileShape ts = nvfp4::tile_shape(plan->cfg);
     plan->tile_m = ts.tile_m;
     plan->tile_n = ts.tile_n;
-    plan->split_k = 1;
-    plan->prefix.assign(num_groups + 1, 0);
-    long long total = 0;
-    int max_ktiles = 0;
-    for (int g = 0; g < num_groups; ++g) {
-        const nvfp4_problem &p = problems[g];
-        long long t = 0;
-        if (!empty_output(p)) {
-            t = (long long)((p.M + ts.tile_m - 1) / ts.tile_m) *
-                (long long)((p.N + ts.tile_n - 1) / ts.tile_n);
-            max_ktiles = std::max(max_ktiles, (p.K + ts.tile_k - 1) / ts.tile_k);
-        }
-        total += t;
-        if (total > kMaxWorkgroups)
-            return NVFP4_ERROR_NOT_SUPPORTED;
-        plan->prefix[g + 1] = (int)total;
-    }
     plan->total_tiles = total;
     // Launch order: longest K first, so in-order dispatch is longest-first
     // (groups of equal K keep their order).
@@ -214,13 +262,6 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         if (2 * m4 < m1)
             plan->cfg = nvfp4::kTile128x128K4;
     }
-    // Split K only where the kernel supports it and the tiles alone leave
-    // compute units idle: at most kTargetWorkgroups workgroups in all, so each
-    // runs once, in a single wave of workgroups.
-    // (a slice keeps at least 4 K tiles: half a K tile per wave)
-    if (plan->cfg == nvfp4::kStream64x32 && total > 0 && total * 2 <= kTargetWorkgroups)
-        plan->split_k = (int)std::min<long long>(
-            {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles / 4), (long long)kMaxSplitK});
     plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
     return NVFP4_OK;
 }

@@ -336,6 +336,67 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_tiled_kernel(GroupTable tab)
 
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Last-arriver sum over the K slices of one output tile (split_k > 1).
+// Every workgroup of the tile stores its partial values (kN per thread, at
+// part + split * slice_elems + i * kStride) with agent-scope atomic stores,
+// which stay coherent across the chip's L2 caches without a whole-cache
+// write-back or invalidate; waits until they have completed; then takes a
+// ticket from the tile's counter.  The workgroup that draws the last ticket
+// adds the slices in slice order (so the result does not depend on arrival
+// order), returns true with the sums in v, and resets the counter to zero
+// for the next launch.  The others return false.  Every thread of the
+// workgroup must call it.
+template <int kN, int kStride>
+__device__ inline bool add_slices(float (&v)[kN], float *part, int slice_elems, int S, int split,
+                                  int *counter, int *s_last)
+{
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        __hip_atomic_store(part + (long)split * slice_elems + i * kStride, v[i], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    if (!*s_last)
+        return false;
+    // slices in batches whose loads are all in flight before the first add
+    constexpr int kBatch = 32 / kN;
+    float t[kN];
+    for (int s0 = 0; s0 < S; s0 += kBatch) {
+        float x[kBatch][kN];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int sl = s0 + b;
+            if (sl < S && sl != split) {
+#pragma unroll
+                for (int i = 0; i < kN; ++i)
+                    x[b][i] = __hip_atomic_load(part + (long)sl * slice_elems + i * kStride, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kN; ++i)
+                    x[b][i] = v[i];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            if (s0 + b < S) {
+#pragma unroll
+                for (int i = 0; i < kN; ++i)
+                    t[i] = s0 + b == 0 ? x[b][i] : t[i] + x[b][i];
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        v[i] = t[i];
+    if (threadIdx.x == 0)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 namespace stream {
 constexpr int BM = 64, BN = 32, BK = 256;
 constexpr int kThreads = 512;
@@ -366,10 +427,11 @@ struct StreamSlot {
 // bytes of a K tile are one aligned load.  Otherwise they are 8 two-byte
 // loads (K % 32 == 0 makes each pair of blocks wholly inside or past K).
 template <bool kVec>
-__global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float *partials)
+__global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float *partials, int *counters)
 {
     using namespace stream;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kWaveBytes];
+    __shared__ int s_last;
 
     const int S = tab.split_k;
     const int tile = blockIdx.x / S;
@@ -526,8 +588,12 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float 
         sum.w += v.w;
     }
     if (S > 1) {
-        *(float4 *)(partials + ((long)tile * S + split) * kTileElems + e0) = sum;
-        return;
+        // row-major partial tiles, [tile][slice][64][32]
+        float vv[4] = {sum.x, sum.y, sum.z, sum.w};
+        if (!add_slices<4, 1>(vv, partials + (long)tile * S * kTileElems + e0, kTileElems, S, split,
+                              counters + tile, &s_last))
+            return;
+        sum = (float4){vv[0], vv[1], vv[2], vv[3]};
     }
     const int row = row0 + e0 / BN, col = col0 + e0 % BN;
     if (row >= M)
@@ -551,51 +617,287 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float 
     }
 }
 
-// Sums the split_k row-major partial tiles (64 x 32 fp32 each) of one output
-// tile in slice order and writes fp16 C.  Thread -> 4 consecutive columns.
-__global__ __launch_bounds__(256) void reduce_partials_kernel(GroupTable tab, const float *partials)
+// ----------------------------------------------------------------------------
+// Small-M panel kernel: 64 x 64 tile per wave, operands staged through LDS.
+//
+// A workgroup owns a 64 x 64 output tile and a slice of K; its 8 waves split
+// that slice again, each accumulating the whole 64 x 64 tile (four 32 x 32
+// MFMA blocks) over its own share, and the 8 partial tiles are added through
+// LDS at the end.  Per 16-K step a wave decodes four fragments (32 VALU) for
+// four MFMAs, so decode and matrix work are balanced.
+//
+// Global loads are coalesced: per 256-K tile, eight lanes read one row's
+// whole 128-byte line, 8 rows per instruction.  Each wave writes them into a
+// private LDS region (no workgroup barrier in the K loop) and reads them back
+// in MFMA lane order.  LDS rows are 128 bytes with the 16-byte chunk index
+// XORed with (row / 2) % 8, which keeps both the row writes and the MFMA-order
+// reads (16 lanes on 16 rows, same chunk) free of bank conflicts.
+//
+// MFMA step (i, q), i = 0..3, q = 0..3: lane half h supplies dword q of chunk
+// 2i + h of its row, K [64i + 32h + 8q, +8), scale block 4i + 2h + q/2.
+namespace panel {
+constexpr int BM = 64, BN = 64, BK = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = BK / 2;  // 128
+constexpr int kSfBytes = BK / 16;  // 16
+constexpr int kAOff = 0;
+constexpr int kBOff = kAOff + BM * kRowBytes;
+constexpr int kSfaOff = kBOff + BN * kRowBytes;
+constexpr int kSfbOff = kSfaOff + BM * kSfBytes;
+constexpr int kWaveBytes = kSfbOff + BN * kSfBytes; // 18432
+constexpr int kTileElems = BM * BN;
+constexpr int kColStride = BM + 4; // floats per column of a partial tile (padded)
+constexpr int kWaveFloats = BN * kColStride;
+static_assert(kWaves * kWaveBytes <= 160 * 1024, "wave regions fit in LDS");
+static_assert(kWaveFloats * 4 <= kWaveBytes, "partial tiles reuse the wave regions");
+static_assert(kThreads * 8 == kTileElems, "8 outputs per thread in the final sum");
+__device__ inline int swz(int r, int c) { return r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4); }
+} // namespace panel
+
+// One 256-K tile of one wave in registers: rows 8j + lane/8 of A and of B,
+// bytes 16 (lane % 8) of their lines.  Scales travel separately.
+struct PanelSlot {
+    u32x4 a[8];
+    u32x4 b[8];
+};
+
+// kVec: K % 256 == 0 and both scale arrays 16-byte aligned.  Then a wave
+// fetches the scales of four K tiles at once, 64 contiguous bytes of 16 rows
+// per instruction (lane l: row 16 i + l / 4, tile l % 4), and each tile's
+// 16 bytes per row move to LDS when the tile does.  Otherwise the scales of
+// each K tile are single-byte loads (lane l: row l), each masked against the
+// row's K / 16 blocks.
+//
+// With split_k > 1 every workgroup of a tile stores its partial tile, then
+// takes a ticket from the tile's counter; the last to arrive adds all
+// partial tiles in slice order (so the result does not depend on arrival
+// order), writes C and resets the counter to zero for the next launch.
+template <bool kVec>
+__global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable tab, float *partials, int *counters)
 {
-    using namespace stream;
-    const long e = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
-    const int tile = (int)(e / kTileElems);
-    const int idx = (int)(e - (long)tile * kTileElems);
-    if (tile >= tab.prefix[tab.num_groups])
-        return;
+    using namespace panel;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kWaveBytes];
+    __shared__ int s_last;
+
     const int S = tab.split_k;
+    const int tile = blockIdx.x / S;
+    const int split = blockIdx.x - tile * S;
     const int gi = find_group(tab, tile);
     const GemmDesc &d = tab.g[gi];
     const int r = tile - tab.prefix[gi];
-    const int tm = r % d.tiles_m, tn = r / d.tiles_m;
+    const int tm = r % d.tiles_m;
+    const int tn = r / d.tiles_m;
+    const int M = d.M, N = d.N, K = d.K;
+    const int row0 = tm * BM, col0 = tn * BN;
 
-    const float *src = partials + (long)tile * S * kTileElems + idx;
-    float4 acc = *(const float4 *)src;
-    for (int s = 1; s < S; ++s) {
-        const float4 v = *(const float4 *)(src + (long)s * kTileElems);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    const int kb_row = K / 2;
+    const int ks_row = K / 16;
+    const int nkt = (K + BK - 1) / BK;
+    const int s0 = (int)((long)split * nkt / S), s1 = (int)((long)(split + 1) * nkt / S);
+    const int kt0 = s0 + (s1 - s0) * wave / kWaves;
+    const int kt1 = s0 + (s1 - s0) * (wave + 1) / kWaves;
+
+    // rows past M / N read as zero (beyond num_records)
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
+
+    const int lrow = lane >> 3, c16 = lane & 7;
+    const uint32_t line_off = (uint32_t)(lrow * kb_row + c16 * 16);
+    const int grow = lane >> 2, gtile = lane & 3; // scale-group lane roles
+    const uint32_t group_off = (uint32_t)(grow * ks_row + gtile * kSfBytes);
+
+    auto load = [&](PanelSlot &s, int kt) {
+        const int kb = kt * kRowBytes;
+        // a 16-byte chunk is wholly inside or past the row's K / 2 bytes
+        const bool cin = kt < kt1 && (kb + c16 * 16) < kb_row;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = cin ? line_off + (uint32_t)(8 * j * kb_row + kb) : kOutOfRange;
+            s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+            s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+        }
+    };
+    // vector path: scales of K tiles kt .. kt + 3 (tiles past this wave's
+    // range read as zero)
+    u32x4 gsa[4], gsb[4];
+    auto load_group = [&](int kt) {
+        const bool live = kt + gtile < kt1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = live ? group_off + (uint32_t)(16 * i * ks_row + kt * kSfBytes) : kOutOfRange;
+            gsa[i] = __builtin_amdgcn_raw_buffer_load_b128(rSA, off, 0, 0);
+            gsb[i] = __builtin_amdgcn_raw_buffer_load_b128(rSB, off, 0, 0);
+        }
+    };
+    // general path: scales of K tile kt, row lane
+    u32x4 tsa, tsb;
+    auto load_bytes = [&](int kt) {
+        const int ks = kt * kSfBytes;
+        const bool live = kt < kt1;
+        uint32_t va[4] = {0, 0, 0, 0}, vb[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bool ok = live && (ks + i) < ks_row;
+            const uint32_t off = ok ? (uint32_t)(lane * ks_row + ks + i) : kOutOfRange;
+            va[i >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSA, off, 0, 0) << (8 * (i & 3));
+            vb[i >> 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSB, off, 0, 0) << (8 * (i & 3));
+        }
+        tsa = (u32x4){va[0], va[1], va[2], va[3]};
+        tsb = (u32x4){vb[0], vb[1], vb[2], vb[3]};
+    };
+
+    uint8_t *wl = lds + wave * kWaveBytes; // this wave's region
+
+    // data of the tile in `s` and its scales (group slot u on the vector path)
+    auto put = [&](const PanelSlot &s, int u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            *(u32x4 *)(wl + kAOff + swz(8 * j + lrow, c16)) = s.a[j];
+            *(u32x4 *)(wl + kBOff + swz(8 * j + lrow, c16)) = s.b[j];
+        }
+        if (kVec) {
+            if (gtile == u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    *(u32x4 *)(wl + kSfaOff + (16 * i + grow) * kSfBytes) = gsa[i];
+                    *(u32x4 *)(wl + kSfbOff + (16 * i + grow) * kSfBytes) = gsb[i];
+                }
+            }
+        } else {
+            *(u32x4 *)(wl + kSfaOff + lane * kSfBytes) = tsa;
+            *(u32x4 *)(wl + kSfbOff + lane * kSfBytes) = tsb;
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = (f32x16){};
+    const uint32_t sh = h * 16;
+
+    auto compute = [&]() {
+        u32x4 sa[2], sb[2]; // the 16 scale bytes of rows 32 o + l32
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            sa[o] = *(const u32x4 *)(wl + kSfaOff + (32 * o + l32) * kSfBytes);
+            sb[o] = *(const u32x4 *)(wl + kSfbOff + (32 * o + l32) * kSfBytes);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 pa[2], pb[2];
+            half2_t ca[2], cb[2]; // blocks 4i + 2h (.x) and 4i + 2h + 1 (.y)
+#pragma unroll
+            for (int o = 0; o < 2; ++o) {
+                pa[o] = *(const u32x4 *)(wl + kAOff + swz(32 * o + l32, 2 * i + h));
+                pb[o] = *(const u32x4 *)(wl + kBOff + swz(32 * o + l32, 2 * i + h));
+                ca[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[o][i] >> sh, 1.0f, false);
+                cb[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[o][i] >> sh, 1.0f, false);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                half8_t fa[2], fb[2];
+#pragma unroll
+                for (int o = 0; o < 2; ++o) {
+                    fa[o] = decode8(pa[o][q], q < 2 ? bcast_lo(ca[o]) : bcast_hi(ca[o]));
+                    fb[o] = decode8(pb[o][q], q < 2 ? bcast_lo(cb[o]) : bcast_hi(cb[o]));
+                }
+#pragma unroll
+                for (int oa = 0; oa < 2; ++oa)
+#pragma unroll
+                    for (int ob = 0; ob < 2; ++ob)
+                        acc[oa][ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[oa], fb[ob], acc[oa][ob], 0, 0, 0);
+            }
+        }
+    };
+
+    if (kt1 > kt0) {
+        PanelSlot x;
+        load(x, kt0);
+        if (kVec)
+            load_group(kt0);
+        else
+            load_bytes(kt0);
+        SCHED_FENCE();
+        // four K tiles per trip, one per scale-group slot; steps past kt1 only
+        // move zeros (their loads are out of range) and skip the compute
+        for (int t = kt0; t < kt1; t += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                put(x, u);
+                SCHED_FENCE();
+                load(x, t + u + 1);
+                if (kVec) {
+                    if (u == 3)
+                        load_group(t + 4);
+                } else {
+                    load_bytes(t + u + 1);
+                }
+                SCHED_FENCE();
+                if (t + u < kt1)
+                    compute();
+                SCHED_FENCE();
+            }
+        }
     }
-    const int row = tm * BM + idx / BN;
-    const int col = tn * BN + idx % BN;
-    if (row >= d.M)
+
+    // every wave is done with its staging region before the partial tiles
+    // (which overlap other waves' regions) are written
+    __syncthreads();
+    float *red = (float *)lds;
+    // column-major with padded columns: lane l holds rows 32 oa + 8 g + 4 h
+    // + (0..3) of column 32 ob + l % 32
+    float *mine = red + wave * kWaveFloats;
+#pragma unroll
+    for (int oa = 0; oa < 2; ++oa)
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(float4 *)(mine + (32 * ob + l32) * kColStride + 32 * oa + 8 * g + 4 * h) =
+                    (float4){acc[oa][ob][4 * g], acc[oa][ob][4 * g + 1], acc[oa][ob][4 * g + 2], acc[oa][ob][4 * g + 3]};
+    __syncthreads();
+
+    // thread -> column n = tid % 64, rows 8 (tid / 64) .. + 7, summed in wave order
+    const int n = tid & 63, m0 = (tid >> 6) * 8;
+    float v[8];
+    {
+        const float4 p = *(const float4 *)(red + n * kColStride + m0);
+        const float4 q = *(const float4 *)(red + n * kColStride + m0 + 4);
+        v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+        v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+    }
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        const float4 p = *(const float4 *)(red + w * kWaveFloats + n * kColStride + m0);
+        const float4 q = *(const float4 *)(red + w * kWaveFloats + n * kColStride + m0 + 4);
+        v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+        v[4] += q.x; v[5] += q.y; v[6] += q.z; v[7] += q.w;
+    }
+    if (S > 1) {
+        // row-major partial tiles, [tile][slice][64][64]
+        if (!add_slices<8, BN>(v, partials + (long)tile * S * kTileElems + m0 * BN + n, kTileElems, S, split,
+                               counters + tile, &s_last))
+            return;
+    }
+    const int col = col0 + n;
+    if (col >= N)
         return;
-    uint16_t *dst = d.C + (long)row * d.N + col;
-    const uint16_t v0 = __builtin_bit_cast(uint16_t, (_Float16)acc.x);
-    const uint16_t v1 = __builtin_bit_cast(uint16_t, (_Float16)acc.y);
-    const uint16_t v2 = __builtin_bit_cast(uint16_t, (_Float16)acc.z);
-    const uint16_t v3 = __builtin_bit_cast(uint16_t, (_Float16)acc.w);
-    if (col + 4 <= d.N && (((uintptr_t)dst) & 7) == 0) {
-        *(u32x2 *)dst = (u32x2){(uint32_t)v0 | ((uint32_t)v1 << 16), (uint32_t)v2 | ((uint32_t)v3 << 16)};
-    } else {
-        if (col < d.N)
-            dst[0] = v0;
-        if (col + 1 < d.N)
-            dst[1] = v1;
-        if (col + 2 < d.N)
-            dst[2] = v2;
-        if (col + 3 < d.N)
-            dst[3] = v3;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = row0 + m0 + i;
+        if (row < M)
+            d.C[(long)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v[i]);
     }
 }
 
@@ -608,28 +910,33 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
     const int total = tiles * table.split_k;
     if (total <= 0)
         return hipSuccess;
+    // workspace: tile counters, then the partial tiles
+    int *counters = (int *)workspace;
+    float *partials = workspace ? (float *)((char *)workspace + kCounterBytes) : nullptr;
+    if (table.split_k > 1 && (workspace == nullptr || tiles > kMaxSplitTiles))
+        return hipErrorInvalidValue;
+    void *args[] = {const_cast<GroupTable *>(&table), &partials, &counters};
     switch (cfg) {
     case kStream64x32: {
-        float *partials = (float *)workspace;
-        void *args[] = {const_cast<GroupTable *>(&table), &partials};
         bool vec = true;
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % stream::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
         const void *fn = vec ? (const void *)gemm_stream_kernel<true> : (const void *)gemm_stream_kernel<false>;
-        hipError_t e = hipLaunchKernel(fn, dim3(total), dim3(stream::kThreads), args, 0, stream);
-        if (e != hipSuccess || table.split_k == 1)
-            return e;
-        const long threads = (long)tiles * stream::kTileElems / 4;
-        const float *cpart = partials;
-        void *rargs[] = {const_cast<GroupTable *>(&table), &cpart};
-        return hipLaunchKernel((const void *)reduce_partials_kernel, dim3((unsigned)((threads + 255) / 256)),
-                               dim3(256), rargs, 0, stream);
+        return hipLaunchKernel(fn, dim3(total), dim3(stream::kThreads), args, 0, stream);
+    }
+    case kPanel64x64: {
+        bool vec = true;
+        for (int g = 0; g < table.num_groups; ++g)
+            vec = vec && (table.g[g].K % panel::BK) == 0 &&
+                  ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
+        const void *fn = vec ? (const void *)gemm_panel_kernel<true> : (const void *)gemm_panel_kernel<false>;
+        return hipLaunchKernel(fn, dim3(total), dim3(panel::kThreads), args, 0, stream);
     }
     case kTile128x128K4:
     case kTile128x128:
     default: {
-        void *args[] = {const_cast<GroupTable *>(&table)};
+        void *targs[] = {const_cast<GroupTable *>(&table)};
         bool vec = true;
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % tiled::BK) == 0 &&
@@ -637,7 +944,7 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         const bool four = cfg == kTile128x128K4;
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
                               : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);
-        return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
+        return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), targs, 0, stream);
     }
     }
 }

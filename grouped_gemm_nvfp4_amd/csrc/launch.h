@@ -39,6 +39,7 @@ enum TileConfig : int {
     kTile128x128 = 0,   // one wave per workgroup owning the whole 128 x 128 tile
     kStream64x32 = 1,   // 8 waves split K; each streams its own share; K may be split
     kTile128x128K4 = 2, // 128 x 128 tile, four waves splitting its K, sums added in LDS
+    kPanel64x64 = 3,    // 8 waves split K, each owning the 64 x 64 tile; K may be split
 };
 
 struct TileShape {
@@ -50,6 +51,8 @@ inline TileShape tile_shape(TileConfig c)
     switch (c) {
     case kStream64x32:
         return {64, 32, 256};
+    case kPanel64x64:
+        return {64, 64, 256};
     case kTile128x128K4:
     case kTile128x128:
     default:
@@ -64,11 +67,15 @@ inline long long partial_elems(TileConfig c)
     return (long long)t.tile_m * t.tile_n;
 }
 
-// Device workspace one launch of `table` needs (bytes): the fp32 partial sums
-// of every (tile, K slice) when split_k > 1, else nothing.
+// Device workspace of a K-split launch (bytes): kMaxSplitTiles tile counters
+// (zero when the workspace is allocated; a kernel that uses them leaves them
+// zero), then the fp32 partial sums of every (tile, K slice).  K is split only
+// when a launch has at most kMaxSplitTiles tiles.
+constexpr int kMaxSplitTiles = 128;
+constexpr long long kCounterBytes = kMaxSplitTiles * 4;
 inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k)
 {
-    return split_k > 1 ? total_tiles * split_k * partial_elems(c) * 4 : 0;
+    return split_k > 1 ? kCounterBytes + total_tiles * split_k * partial_elems(c) * 4 : 0;
 }
 
 // Launches one grouped pass (table already filled, prefix included).  With

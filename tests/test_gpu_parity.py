@@ -126,6 +126,39 @@ def test_tiled_variants(lib, M, N, K, kernel):
         check_sampled(got, p, 91, "tiled %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K,split", [
+    (64, 6144, 8192, 2),    # scale groups of four K tiles, K split in two
+    (64, 16384, 4096, 1),   # no split
+    (48, 12288, 4128, 1),   # K % 256 != 0: byte scale loads, ragged last K tile
+    (64, 6400, 8224, 2),    # byte scale loads with a K split
+    (33, 7000, 8192, 2),    # ragged M and N
+])
+def test_panel_shapes(lib, M, N, K, split):
+    """M <= 64 with enough 64 x 64 tiles (and K slices) to fill the chip takes
+    the panel kernel."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["tile_n"] == 64 and info["split_k"] == split
+    p = inputs.draw_problems(5000 + M + K, [(M, N, K)])[0]
+    check_full(lib, p, "panel %dx%dx%d split %d" % (M, N, K, split))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 6144, 8192), (40, 500, 1024), (200, 136, 512)])
+def test_scale_pointers_at_odd_offsets(lib, M, N, K):
+    """Scale arrays that start at an odd byte address take the byte-load
+    paths of every kernel."""
+    p = inputs.draw_problems(5100 + M, [(M, N, K)])[0]
+    A, _, B, _, C = dev_problem(p)
+    sfa = torch.zeros(p.SFA.size + 1, dtype=torch.uint8, device="cuda")
+    sfb = torch.zeros(p.SFB.size + 1, dtype=torch.uint8, device="cuda")
+    sfa[1:] = to_dev(p.SFA.reshape(-1))
+    sfb[1:] = to_dev(p.SFB.reshape(-1))
+    assert sfa[1:].data_ptr() % 2 == 1
+    lib.nvfp4_gemm(A, sfa[1:], B, sfb[1:], C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(bits(C), c16, bound, "odd scale pointers %dx%dx%d" % (M, N, K))
+
+
 def test_all_ones_gives_exactly_K(lib):
     M, N, K = 130, 70, 7168
     ones = inputs.Problem(M, N, K, np.full((M, K // 2), 0x22, np.uint8),
@@ -236,6 +269,19 @@ def test_group_small_m_split_k(lib):
             continue
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "small-M group %d" % i)
+
+
+def test_group_small_m_panel(lib):
+    """Small-M groups whose 64 x 64 tiles fill the chip take the panel kernel
+    with a K split; ragged N and M in some groups."""
+    shapes = [(64, 2048, 8192), (17, 2000, 8192), (64, 2048, 4096), (50, 1900, 8192)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["tile_n"] == 64 and info["split_k"] > 1
+    probs = inputs.draw_problems(38, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "panel group %d" % i)
 
 
 def test_group_single_group_matches_gemm(lib):
