@@ -14,13 +14,22 @@ exceeds the 256 MiB Infinity Cache plus the L2s, so each step reads its
 operands from HBM rather than from a cache warmed by the previous step.
 
 Prints one JSON line: TFLOPS = sum 2*M*N*K / time, the roofline of the kernel
-(algorithmic bytes or flops per launch over its mean launch duration, timed
-with HIP events on the launch stream), and the CPU oracle's throughput on a
-bounded sample of the same workload.
+(algorithmic bytes or flops per launch over its mean launch duration: the
+timed region measured with HIP events on the launch stream, divided by the
+number of steps), and the CPU oracle's throughput on a bounded sample of the
+same workload.  The roofline's "traffic" (HBM bytes per launch from the
+FETCH_SIZE and WRITE_SIZE counters) comes from profiles/hbm_traffic.txt and is
+reported only while the kernel source it was measured on is unchanged.
+
+    python bench.py --copy-probe BYTES
+
+runs a plain device-to-device copy of BYTES bytes a few times and exits: under
+rocprofv3 --pmc it calibrates the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -54,7 +63,39 @@ def parse():
                     help="operand copies to cycle over (0: enough to exceed the caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0: skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "grouped_gemm_nvfp4_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch recorded for this workload, if they were measured
+    on the current kernel source (lines: workload sha256 bytes)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(KERNEL_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split("#")[0].split()
+            if len(parts) == 3 and parts[0] == workload and parts[1] == sha:
+                return float(parts[2])
+    return None
+
+
+def copy_probe(nbytes):
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)  # reads 4n bytes, writes 4n bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "launches": 5}))
 
 
 def cpu_baseline(probs, target_s):
@@ -84,13 +125,16 @@ def cpu_baseline(probs, target_s):
     f_cal, _ = run(frac)
     rate = f_cal / max(1e-9, time.perf_counter() - t0)
     frac = min(1.0, target_s * rate / total_flops)
-    reps = max(1, int(round(target_s * rate / total_flops))) if frac >= 1.0 else 1
-    done = 0
+    # whole passes (or one partial pass) until about target_s has elapsed
+    done, reps = 0, 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while True:
         f, rows = run(frac)
         done += f
-    dt = time.perf_counter() - t0
+        reps += 1
+        dt = time.perf_counter() - t0
+        if frac < 1.0 or dt >= target_s:
+            break
     if frac >= 1.0:
         sample = "the whole workload, %d pass(es), %.1f s" % (reps, dt)
     else:
@@ -102,6 +146,9 @@ def cpu_baseline(probs, target_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -159,18 +206,17 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_start.record(stream)
     for i in range(K):
-        ev0[i].record(stream)
         step(i)
-        ev1[i].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = np.array([a.elapsed_time(z) for a, z in zip(ev0, ev1)])
-    kern_s = float(np.mean(launch_ms)) / 1e3
+    kern_s = e_start.elapsed_time(e_end) / 1e3 / K
 
     # same operands every step (cache-warm), for context only
     torch.cuda.synchronize()
@@ -190,14 +236,12 @@ def main():
     small_m = (not wl.grouped) and probs[0].M <= 128
     if small_m:
         roof = {"bound": "hbm", "achieved": kern_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": kern_gbps / PEAK_HBM_GBPS, "traffic": None}
+                "frac": kern_gbps / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name)}
     else:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic(wl.name)}
     roof["per_launch"] = {"flops": flops, "algorithmic_bytes": alg_bytes,
-                          "mean_launch_us": kern_s * 1e6,
-                          "p10_us": float(np.percentile(launch_ms, 10)) * 1e3,
-                          "p90_us": float(np.percentile(launch_ms, 90)) * 1e3}
+                          "mean_launch_us": kern_s * 1e6}
 
     cpu = None
     if args.cpu_seconds > 0:
