@@ -218,6 +218,23 @@ def main():
     wall = time.perf_counter() - t0
     kern_s = e_start.elapsed_time(e_end) / 1e3 / K
 
+    # per-launch distribution (a separate pass: an event pair around each
+    # call), and the host time of one call (enqueue only, no synchronisation)
+    nd = min(K, 100)
+    d0 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+    d1 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+    host = []
+    torch.cuda.synchronize()
+    for i in range(nd):
+        d0[i].record(stream)
+        h0 = time.perf_counter()
+        step(i)
+        host.append(time.perf_counter() - h0)
+        d1[i].record(stream)
+    torch.cuda.synchronize()
+    each_us = np.array([a.elapsed_time(z) for a, z in zip(d0, d1)]) * 1e3
+    host_us = float(np.median(host)) * 1e6
+
     # same operands every step (cache-warm), for context only
     torch.cuda.synchronize()
     w0 = torch.cuda.Event(enable_timing=True)
@@ -241,7 +258,9 @@ def main():
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic(wl.name)}
     roof["per_launch"] = {"flops": flops, "algorithmic_bytes": alg_bytes,
-                          "mean_launch_us": kern_s * 1e6}
+                          "mean_launch_us": kern_s * 1e6,
+                          "event_pair_us_p10_p50_p90": [float(np.percentile(each_us, q)) for q in (10, 50, 90)],
+                          "host_call_us_median": host_us}
 
     cpu = None
     if args.cpu_seconds > 0:

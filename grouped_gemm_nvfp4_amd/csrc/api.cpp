@@ -239,7 +239,12 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     std::stable_sort(plan->order.begin(), plan->order.end(), [&](int a, int b) {
         return problems[a].K > problems[b].K;
     });
-    if (plan->cfg == nvfp4::kTile128x128 && total > 0 && total < 4 * kWaveSlots) {
+    // (each of the four waves needs at least one K tile of every group)
+    bool four_ok = true;
+    for (int g = 0; g < num_groups; ++g)
+        if (!empty_output(problems[g]) && problems[g].K < 4 * ts.tile_k)
+            four_ok = false;
+    if (plan->cfg == nvfp4::kTile128x128 && four_ok && total > 0 && total < 4 * kWaveSlots) {
         // Few tiles: compare one wave per tile (kWaveSlots slots) with four
         // waves splitting each tile's K (kWaveSlots / 4 slots, a quarter of the
         // K tiles each, plus about 3% for adding the sums).
@@ -256,7 +261,8 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         // Measured: per K tile the four-wave form is slower than four
         // independent one-wave workgroups (the 8-group and 2-group workloads
         // ran 10-17% slower with it), so it is taken only where the model
-        // promises at least a factor of two: few, long tiles.
+        // promises at least a factor of two: few, long tiles (there it wins
+        // 1.4-3.4x: 256x384x1024, 1000x520x1184, 512x512x16384).
         const long long m1 = list_makespan(g1, kWaveSlots);
         const long long m4 = list_makespan(g4, kWaveSlots / 4) * 103 / 100;
         if (2 * m4 < m1)

@@ -37,6 +37,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 // Raw (unstrided) buffer resource: loads at offsets >= num_records return 0.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -284,13 +286,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_tiled_kernel(GroupTable tab)
             __syncthreads();
             if (wave < give_lo) {
                 const float *src = red + wave * kAccFloats + lane;
+                // one 16-value block at a time (fences keep the loads of
+                // later blocks from being hoisted: no spill next to 256
+                // live accumulators)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 4; ++j) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e)
                             acc[i][j][e] += src[((i * 4 + j) * 16 + e) * 64];
+                        SCHED_FENCE();
+                    }
             }
             __syncthreads();
         }
@@ -334,7 +341,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_tiled_kernel(GroupTable tab)
     }
 }
 
-#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Last-arriver sum over the K slices of one output tile (split_k > 1).
 // Every workgroup of the tile stores its partial values (kN per thread, at
