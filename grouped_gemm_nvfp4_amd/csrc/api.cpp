@@ -61,6 +61,8 @@ struct Plan {
     std::vector<int> order;  // launch order of the groups (longest K first)
     long long total_tiles;
     long long workspace_bytes;
+    int sk_workgroups = 0;   // stream-K grid
+    long long sk_units = 0;  // stream-K (tile, K tile) units
 };
 
 // Workgroup slots of an MI355X: 256 CUs x 4 SIMDs for one-wave workgroups.
@@ -187,6 +189,48 @@ int small_m_split(long long total, int max_ktiles, int min_ktiles)
         {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles / min_ktiles), (long long)kMaxSplitK});
 }
 
+// Stream-K for one-wave 128 x 128 tiles: P workgroups (one per SIMD at most,
+// at least kMinUnitsPerWorkgroup K tiles each) take equal shares of the
+// launch's (tile, K tile) units.  Each shared tile costs its contributors a
+// write-through store of a 64 KiB partial tile and its last contributor the
+// serial read of all of them: measured, about kFixupUnits K tiles of time plus
+// half a K tile per contributor, and more when a thousand workgroups do it at
+// once (the 8-group MoE and 2-group workloads ran 1.2x and 1.7x slower with
+// it).  So it is taken only for at most kMaxStreamKTiles tiles and when the
+// model -- U / P units plus that cost -- beats the four-wave form and is at
+// most 2/3 of the dispatcher's list schedule of whole one-wave tiles
+// (512x512x16384: 113 us four-wave, 86 us stream-K; 256x1024x8192: 67 us
+// four-wave, 73 us stream-K).
+constexpr int kMinUnitsPerWorkgroup = 16;
+constexpr int kFixupUnits = 8;
+constexpr long long kMaxStreamKTiles = 256;
+
+// Stream-K estimate in quarter K tiles (the unit of the makespans below), or
+// -1 where stream-K does not apply; sets *P to its grid.
+long long stream_k_makespan(const nvfp4_problem *problems, const Plan &plan, const nvfp4::TileShape &ts, int *P_out)
+{
+    const int num_groups = (int)plan.prefix.size() - 1;
+    int launched = 0;
+    for (int g = 0; g < num_groups; ++g)
+        launched += plan.prefix[g + 1] > plan.prefix[g];
+    if (plan.total_tiles > kMaxStreamKTiles || launched > nvfp4::kMaxGroupsPerLaunch)
+        return -1;
+    long long units = 0, max_kt = 1;
+    for (int gi : plan.order) {
+        const long long t = plan.prefix[gi + 1] - plan.prefix[gi];
+        if (t == 0)
+            continue;
+        const long long kt = std::max(1, (problems[gi].K + ts.tile_k - 1) / ts.tile_k);
+        units += t * kt;
+        max_kt = std::max(max_kt, kt);
+    }
+    const long long P = std::max(1LL, std::min<long long>(kWaveSlots, units / kMinUnitsPerWorkgroup));
+    const long long per_wg = (units + P - 1) / P;
+    const long long contributors = (max_kt + per_wg - 1) / per_wg + 1;
+    *P_out = (int)P;
+    return 4 * (per_wg + kFixupUnits + (contributors + 1) / 2);
+}
+
 nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan)
 {
     if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS)
@@ -244,10 +288,11 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     for (int g = 0; g < num_groups; ++g)
         if (!empty_output(problems[g]) && problems[g].K < 4 * ts.tile_k)
             four_ok = false;
-    if (plan->cfg == nvfp4::kTile128x128 && four_ok && total > 0 && total < 4 * kWaveSlots) {
-        // Few tiles: compare one wave per tile (kWaveSlots slots) with four
-        // waves splitting each tile's K (kWaveSlots / 4 slots, a quarter of the
-        // K tiles each, plus about 3% for adding the sums).
+    if (plan->cfg == nvfp4::kTile128x128 && total > 0 && total < 4 * kWaveSlots) {
+        // Few tiles: compare one wave per tile (kWaveSlots slots), four waves
+        // splitting each tile's K (kWaveSlots / 4 slots, a quarter of the K
+        // tiles each, plus about 3% for adding the sums) and stream-K, all in
+        // quarter K tiles.
         std::vector<std::pair<long long, long long>> g1, g4;
         for (int gi : plan->order) {
             const nvfp4_problem &p = problems[gi];
@@ -258,17 +303,28 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
             g1.emplace_back(t, 4 * kt);
             g4.emplace_back(t, kt + 1);
         }
+        const long long m1 = list_makespan(g1, kWaveSlots);
+        const long long m4 = four_ok ? list_makespan(g4, kWaveSlots / 4) * 103 / 100 : -1;
+        int P = 0;
+        const long long msk = stream_k_makespan(problems, *plan, ts, &P);
         // Measured: per K tile the four-wave form is slower than four
         // independent one-wave workgroups (the 8-group and 2-group workloads
         // ran 10-17% slower with it), so it is taken only where the model
         // promises at least a factor of two: few, long tiles (there it wins
         // 1.4-3.4x: 256x384x1024, 1000x520x1184, 512x512x16384).
-        const long long m1 = list_makespan(g1, kWaveSlots);
-        const long long m4 = list_makespan(g4, kWaveSlots / 4) * 103 / 100;
-        if (2 * m4 < m1)
+        if (msk >= 0 && 3 * msk <= 2 * m1 && (m4 < 0 || msk < m4)) {
+            plan->cfg = nvfp4::kTile128x128SK;
+            plan->sk_workgroups = P;
+            long long units = 0;
+            for (int gi : plan->order)
+                units += (long long)(plan->prefix[gi + 1] - plan->prefix[gi]) *
+                         std::max(1, (problems[gi].K + ts.tile_k - 1) / ts.tile_k);
+            plan->sk_units = units;
+        } else if (m4 >= 0 && 2 * m4 < m1) {
             plan->cfg = nvfp4::kTile128x128K4;
+        }
     }
-    plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
+    plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k, plan->sk_workgroups);
     return NVFP4_OK;
 }
 
@@ -276,12 +332,13 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
 {
     info->kernel = plan.total_tiles == 0 ? 0
                    : plan.split_k > 1 ? 2
-                   : plan.cfg == nvfp4::kTile128x128K4 ? 3 : 1;
+                   : plan.cfg == nvfp4::kTile128x128K4 ? 3
+                   : plan.cfg == nvfp4::kTile128x128SK ? 4 : 1;
     info->tile_m = plan.tile_m;
     info->tile_n = plan.tile_n;
     info->split_k = plan.split_k;
     info->total_tiles = (int)plan.total_tiles;
-    info->workgroups = (int)(plan.total_tiles * plan.split_k);
+    info->workgroups = plan.cfg == nvfp4::kTile128x128SK ? plan.sk_workgroups : (int)(plan.total_tiles * plan.split_k);
     info->workspace_bytes = plan.workspace_bytes;
 }
 
@@ -306,7 +363,8 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
             return NVFP4_OK;
         table.num_groups = n;
         // launches of one call share the workspace: stream order keeps them apart
-        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, workspace, stream);
+        table.units = (int)plan.sk_units;
+        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, workspace, plan.sk_workgroups, stream);
         n = 0;
         table.prefix[0] = 0;
         return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;

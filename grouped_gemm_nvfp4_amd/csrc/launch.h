@@ -30,6 +30,7 @@ constexpr int kMaxGroupsPerLaunch = 64;
 struct GroupTable {
     int num_groups;
     int split_k;                         // K slices per tile (1: no split)
+    int units;                           // stream-K: (tile, K tile) units of the launch
     int prefix[kMaxGroupsPerLaunch + 1]; // in output tiles
     GemmDesc g[kMaxGroupsPerLaunch];
 };
@@ -40,6 +41,7 @@ enum TileConfig : int {
     kStream64x32 = 1,   // 8 waves split K; each streams its own share; K may be split
     kTile128x128K4 = 2, // 128 x 128 tile, four waves splitting its K, sums added in LDS
     kPanel64x64 = 3,    // 8 waves split K, each owning the 64 x 64 tile; K may be split
+    kTile128x128SK = 4, // one-wave 128 x 128 tiles, stream-K: equal (tile, K tile) shares
 };
 
 struct TileShape {
@@ -54,6 +56,7 @@ inline TileShape tile_shape(TileConfig c)
     case kPanel64x64:
         return {64, 64, 256};
     case kTile128x128K4:
+    case kTile128x128SK:
     case kTile128x128:
     default:
         return {128, 128, 128};
@@ -67,21 +70,23 @@ inline long long partial_elems(TileConfig c)
     return (long long)t.tile_m * t.tile_n;
 }
 
-// Device workspace of a K-split launch (bytes): kMaxSplitTiles tile counters
-// (zero when the workspace is allocated; a kernel that uses them leaves them
-// zero), then the fp32 partial sums of every (tile, K slice).  K is split only
-// when a launch has at most kMaxSplitTiles tiles.
-constexpr int kMaxSplitTiles = 128;
+// Device workspace of a K-split or stream-K launch (bytes): kMaxSplitTiles
+// tile counters (zero when the workspace is allocated; a kernel that uses
+// them leaves them zero), then the fp32 partial tiles: of every (tile, K
+// slice) for a K split, two per workgroup for stream-K.  Such launches have at
+// most kMaxSplitTiles tiles.
+constexpr int kMaxSplitTiles = 4096;
 constexpr long long kCounterBytes = kMaxSplitTiles * 4;
-inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k)
+inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k, int sk_workgroups)
 {
+    if (c == kTile128x128SK)
+        return kCounterBytes + 2LL * sk_workgroups * partial_elems(c) * 4;
     return split_k > 1 ? kCounterBytes + total_tiles * split_k * partial_elems(c) * 4 : 0;
 }
 
-// Launches one grouped pass (table already filled, prefix included).  With
-// split_k > 1 the workspace holds the partial sums; a second kernel on the
-// same stream adds them in K-slice order and writes C.
-hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace,
+// Launches one grouped pass (table already filled, prefix included, units
+// set for stream-K).  sk_workgroups: the stream-K grid (kTile128x128SK only).
+hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, int sk_workgroups,
                           hipStream_t stream);
 
 } // namespace nvfp4

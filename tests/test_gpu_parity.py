@@ -159,6 +159,28 @@ def test_scale_pointers_at_odd_offsets(lib, M, N, K):
     assert_parity(bits(C), c16, bound, "odd scale pointers %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (512, 512, 16384),   # 16 tiles, 2048 units over 128 workgroups
+    (300, 520, 16384),   # 15 ragged tiles
+    (129, 257, 32768),   # 6 tiles, mostly padding rows and columns
+])
+def test_stream_k_shapes(lib, M, N, K):
+    """Few 128 x 128 tiles with long K: workgroups take equal shares of the
+    (tile, K tile) units and shared tiles are summed by the last arriver."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == 4 and info["workgroups"] > info["total_tiles"]
+    p = inputs.draw_problems(5200 + M + K, [(M, N, K)])[0]
+    check_full(lib, p, "stream-K %dx%dx%d" % (M, N, K))
+
+
+def test_stream_k_deterministic(lib):
+    """The last arriver adds the partial tiles in workgroup order, so repeated
+    calls agree bit for bit whatever order the workgroups finish in."""
+    p = inputs.draw_problems(5300, [(512, 512, 16384)])[0]
+    runs = [run_gemm(lib, p) for _ in range(3)]
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+
+
 def test_all_ones_gives_exactly_K(lib):
     M, N, K = 130, 70, 7168
     ones = inputs.Problem(M, N, K, np.full((M, K // 2), 0x22, np.uint8),
@@ -282,6 +304,24 @@ def test_group_small_m_panel(lib):
     for i, (p, got) in enumerate(zip(probs, outs)):
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "panel group %d" % i)
+
+
+def test_group_stream_k_mixed(lib):
+    """A stream-K grouped launch with ragged M and N, different K per group,
+    a K = 0 group (zero C) and an empty group."""
+    shapes = [(300, 400, 8192), (129, 257, 16384), (200, 100, 0), (0, 64, 256), (256, 384, 8192), (65, 700, 6144)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["kernel"] == 4
+    probs = inputs.draw_problems(39, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "stream-K group %d" % i)
 
 
 def test_group_single_group_matches_gemm(lib):
