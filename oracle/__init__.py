@@ -163,3 +163,43 @@ def group_gemm(problems):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return _load().oracle_num_threads()
+
+
+# ---------------------------------------------------------------- blocked scales
+#
+# The scale layout the pages' kernels consume.  The raw-CUDA page
+# (nvfp4-group-gemm-407526, device kernel, the scale TMA issue) addresses a
+# 128-row tile's scales at (tile * K/64) * 512 bytes and advances 2048 bytes
+# (four 512-byte atoms) per 256-element K step; the single-GEMM page
+# (nvfp4-gemm-125598, `custom_kernel` docstring) gives the permuted scale
+# tensor the shape [32, 4, rest_m, 4, rest_k, l].  Reading: one 512-byte atom
+# holds the scales of 128 rows x 4 consecutive K/16 blocks, and within it the
+# byte of row r (0..127) and block c (0..3) sits at (r % 32) * 16 + (r // 32)
+# * 4 + c; atoms are ordered row tile major, K atom minor.  Rows are padded to
+# a multiple of 128 and K/16 blocks to a multiple of 4 with zero bytes.
+
+
+def blocked_scale_shape(rows: int, K: int):
+    """(row tiles, K atoms, total bytes) of the blocked layout."""
+    rest_m = (rows + 127) // 128
+    rest_k = (K // 16 + 3) // 4
+    return rest_m, rest_k, rest_m * rest_k * 512
+
+
+def scales_to_blocked(sf: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Plain [rows][K/16] scales -> the blocked byte layout (1-D uint8)."""
+    rest_m, rest_k, _ = blocked_scale_shape(rows, K)
+    kb = K // 16
+    padded = np.zeros((rest_m * 128, rest_k * 4), np.uint8)
+    padded[:rows, :kb] = np.asarray(sf, np.uint8).reshape(rows, kb)
+    # [row tile, r // 32, r % 32, K atom, c] -> [row tile, K atom, r % 32, r // 32, c]
+    t = padded.reshape(rest_m, 4, 32, rest_k, 4).transpose(0, 3, 2, 1, 4)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def scales_from_blocked(blocked: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """The blocked byte layout -> plain [rows][K/16] scales."""
+    rest_m, rest_k, nbytes = blocked_scale_shape(rows, K)
+    t = np.asarray(blocked, np.uint8).reshape(-1)[:nbytes].reshape(rest_m, rest_k, 32, 4, 4)
+    padded = t.transpose(0, 3, 2, 1, 4).reshape(rest_m * 128, rest_k * 4)
+    return np.ascontiguousarray(padded[:rows, :K // 16])

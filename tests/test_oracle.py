@@ -361,3 +361,60 @@ def test_parity_rule_accepts_and_rejects():
     assert ulp16(np.array([1.0]))[0] == 2.0 ** -10
     assert ulp16(np.array([0.0]))[0] == 2.0 ** -24
     assert ulp16(np.array([65504.0]))[0] == 32.0
+
+
+# ------------------------------------------------------------ blocked scale layout
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (128, 256), (300, 96), (129, 1056), (512, 7168)])
+def test_blocked_scales_round_trip(rows, K):
+    rng = np.random.default_rng(rows + K)
+    sf = rng.integers(0, 256, (rows, K // 16), dtype=np.uint8)
+    blk = oracle.scales_to_blocked(sf, rows, K)
+    assert blk.size == oracle.blocked_scale_shape(rows, K)[2]
+    assert np.array_equal(oracle.scales_from_blocked(blk, rows, K), sf)
+    # padding bytes are zero: exactly the non-padding bytes carry data
+    assert np.count_nonzero(blk) == np.count_nonzero(sf)
+
+
+def test_blocked_scales_follow_the_pages_atom_addressing():
+    """The raw-CUDA page fetches, for 128-row tile t and 256-K step s, the 2048
+    bytes at (t * K/64) * 512 + s * 2048: they must hold exactly the scales of
+    rows [128 t, 128 t + 128) and blocks [16 s, 16 s + 16)."""
+    rows, K = 384, 2048
+    kb = K // 16
+    # every (row, block) gets a 16-bit identity, carried through the byte
+    # layout as two byte planes (no padding at this size)
+    sf = np.arange(rows * kb, dtype=np.int64).reshape(rows, kb)
+    lo = oracle.scales_to_blocked((sf & 0xFF).astype(np.uint8), rows, K).astype(np.int64)
+    hi = oracle.scales_to_blocked((sf >> 8).astype(np.uint8), rows, K).astype(np.int64)
+    ids = lo | (hi << 8)
+    rest_k = K // 64
+    for t in range(rows // 128):
+        for s in range(K // 256):
+            base = (t * rest_k) * 512 + s * 2048
+            got = set(ids[base:base + 2048].tolist())
+            want = {r * kb + j for r in range(128 * t, 128 * t + 128) for j in range(16 * s, 16 * s + 16)}
+            assert got == want
+
+
+def test_blocked_scales_row_within_atom():
+    """Within one atom, rows r and r + 32 sit 4 bytes apart and rows r, r + 1
+    sit 16 bytes apart ([32, 4, ..., 4, ...]: r % 32 outer, r // 32 next, the
+    block innermost)."""
+    rows, K = 128, 64
+    sf = np.zeros((rows, 4), np.uint8)
+    sf[33, 2] = 7          # r = 33: r % 32 = 1, r // 32 = 1, block 2
+    blk = oracle.scales_to_blocked(sf, rows, K)
+    assert np.flatnonzero(blk).tolist() == [1 * 16 + 1 * 4 + 2]
+
+
+def test_blocked_scales_give_the_same_product():
+    """C computed from scales that went through the blocked layout and back is
+    bitwise the plain-layout C (the layout moves bytes only)."""
+    from grouped_gemm_nvfp4_amd import inputs
+    p = inputs.draw_problems(77, [(130, 70, 320)])[0]
+    sfa = oracle.scales_from_blocked(oracle.scales_to_blocked(p.SFA, p.M, p.K), p.M, p.K)
+    sfb = oracle.scales_from_blocked(oracle.scales_to_blocked(p.SFB, p.N, p.K), p.N, p.K)
+    c1, _, _ = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+    c2, _, _ = oracle.gemm(p.A, sfa, p.B, sfb, p.M, p.N, p.K)
+    assert np.array_equal(c1, c2)
