@@ -63,6 +63,9 @@ def parse():
                     help="operand copies to cycle over (0: enough to exceed the caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0: skip)")
+    ap.add_argument("--scale-layout", choices=("plain", "blocked"), default="plain",
+                    help="scales as [rows][K/16] (default) or in the pages' blocked 512-byte atoms "
+                         "(nvfp4_gemm_blocked / nvfp4_group_gemm_blocked)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     return ap.parse_args()
@@ -180,6 +183,23 @@ def main():
             one.append((A, SFA, B, SFB, C))
         sets.append(one)
 
+    blocked = args.scale_layout == "blocked"
+    if blocked:
+        # the scales of every copy moved into the blocked layout, on the device
+        # by the library itself
+        conv = []
+        for one in sets:
+            c1 = []
+            for (A, SFA, B, SFB, C), p in zip(one, probs):
+                bsa = torch.empty(max(1, g.nvfp4_blocked_scale_bytes(p.M, p.K)), dtype=torch.uint8, device=dev)
+                bsb = torch.empty(max(1, g.nvfp4_blocked_scale_bytes(p.N, p.K)), dtype=torch.uint8, device=dev)
+                g.nvfp4_scales_to_blocked(SFA, bsa, p.M, p.K)
+                g.nvfp4_scales_to_blocked(SFB, bsb, p.N, p.K)
+                c1.append((A, bsa, B, bsb, C))
+            conv.append(c1)
+        torch.cuda.synchronize()
+        sets = conv
+
     # marshal each set once; a step is then a single C call
     calls = []
     for one in sets:
@@ -194,10 +214,12 @@ def main():
                 arr[i] = b.Nvfp4Problem(A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
                                         SFB.data_ptr(), C.data_ptr(), p.M, p.N, p.K)
             calls.append(("group", (arr, len(one), sh)))
+    gemm_fn = lib.nvfp4_gemm_blocked if blocked else lib.nvfp4_gemm
+    group_fn = lib.nvfp4_group_gemm_blocked if blocked else lib.nvfp4_group_gemm
 
     def step(i):
         kind, a = calls[i % len(calls)]
-        rc = lib.nvfp4_gemm(*a) if kind == "gemm" else lib.nvfp4_group_gemm(*a)
+        rc = gemm_fn(*a) if kind == "gemm" else group_fn(*a)
         if rc != 0:
             raise RuntimeError(g.status_string(rc))
 
@@ -253,10 +275,12 @@ def main():
     small_m = (not wl.grouped) and probs[0].M <= 128
     if small_m:
         roof = {"bound": "hbm", "achieved": kern_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": kern_gbps / PEAK_HBM_GBPS, "traffic": measured_traffic(wl.name)}
+                "frac": kern_gbps / PEAK_HBM_GBPS,
+                "traffic": None if blocked else measured_traffic(wl.name)}
     else:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic(wl.name)}
+                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS,
+                "traffic": None if blocked else measured_traffic(wl.name)}
     roof["per_launch"] = {"flops": flops, "algorithmic_bytes": alg_bytes,
                           "mean_launch_us": kern_s * 1e6,
                           "event_pair_us_p10_p50_p90": [float(np.percentile(each_us, q)) for q in (10, 50, 90)],
@@ -281,7 +305,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
                    "shapes_MNK": shapes, "seed": 1000 + args.workload,
-                   "operand_copies": copies},
+                   "operand_copies": copies, "scale_layout": args.scale_layout},
         "roofline": roof,
         "cpu_baseline": cpu,
         "pct_fp4_peak": 100.0 * kern_tflops / PEAK_FP4_TFLOPS,

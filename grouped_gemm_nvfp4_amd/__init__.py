@@ -9,8 +9,13 @@ from ._binding import (  # noqa: F401
     gemm_plan,
     group_gemm_plan,
     load,
+    nvfp4_blocked_scale_bytes,
     nvfp4_gemm,
+    nvfp4_gemm_blocked,
     nvfp4_group_gemm,
+    nvfp4_group_gemm_blocked,
+    nvfp4_scales_from_blocked,
+    nvfp4_scales_to_blocked,
     release_workspaces,
     status_string,
 )

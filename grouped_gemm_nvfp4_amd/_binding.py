@@ -21,6 +21,8 @@ NVFP4_ERROR_LAUNCH = 3
 EXPORTED = [
     "nvfp4_gemm", "nvfp4_group_gemm", "nvfp4_gemm_plan", "nvfp4_group_gemm_plan",
     "nvfp4_release_workspaces", "nvfp4_status_string", "nvfp4_abi_version",
+    "nvfp4_blocked_scale_bytes", "nvfp4_scales_to_blocked", "nvfp4_scales_from_blocked",
+    "nvfp4_gemm_blocked", "nvfp4_group_gemm_blocked",
 ]
 
 
@@ -77,6 +79,16 @@ def load():
     lib.nvfp4_status_string.restype = ctypes.c_char_p
     lib.nvfp4_abi_version.argtypes = []
     lib.nvfp4_abi_version.restype = ci
+    lib.nvfp4_blocked_scale_bytes.argtypes = [ci, ci]
+    lib.nvfp4_blocked_scale_bytes.restype = ctypes.c_longlong
+    lib.nvfp4_scales_to_blocked.argtypes = [vp, vp, ci, ci, vp]
+    lib.nvfp4_scales_to_blocked.restype = ci
+    lib.nvfp4_scales_from_blocked.argtypes = [vp, vp, ci, ci, vp]
+    lib.nvfp4_scales_from_blocked.restype = ci
+    lib.nvfp4_gemm_blocked.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.nvfp4_gemm_blocked.restype = ci
+    lib.nvfp4_group_gemm_blocked.argtypes = [ctypes.POINTER(Nvfp4Problem), ci, vp]
+    lib.nvfp4_group_gemm_blocked.restype = ci
     _lib = lib
     return lib
 
@@ -135,6 +147,34 @@ def nvfp4_group_gemm(problems, stream=None):
             A, SFA, B, SFB, C, M, N, K = p
         arr[i] = _problem(A, SFA, B, SFB, C, M, N, K)
     _check(load().nvfp4_group_gemm(arr, len(problems), _stream_handle(stream)))
+
+
+def nvfp4_gemm_blocked(A, SFA, B, SFB, C, M, N, K, stream=None):
+    """nvfp4_gemm with SFA and SFB in the blocked layout (uint8 device
+    tensors of nvfp4_blocked_scale_bytes(M or N, K) bytes)."""
+    _check(load().nvfp4_gemm_blocked(_ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _ptr(C),
+                                     M, N, K, _stream_handle(stream)))
+
+
+def nvfp4_group_gemm_blocked(problems, stream=None):
+    """nvfp4_group_gemm with blocked scales; ``problems`` as for
+    nvfp4_group_gemm with explicit (A, SFA, B, SFB, C, M, N, K)."""
+    arr = (Nvfp4Problem * max(1, len(problems)))()
+    for i, (A, SFA, B, SFB, C, M, N, K) in enumerate(problems):
+        arr[i] = _problem(A, SFA, B, SFB, C, M, N, K)
+    _check(load().nvfp4_group_gemm_blocked(arr, len(problems), _stream_handle(stream)))
+
+
+def nvfp4_blocked_scale_bytes(rows, K) -> int:
+    return int(load().nvfp4_blocked_scale_bytes(rows, K))
+
+
+def nvfp4_scales_to_blocked(sf, blocked, rows, K, stream=None):
+    _check(load().nvfp4_scales_to_blocked(_ptr(sf), _ptr(blocked), rows, K, _stream_handle(stream)))
+
+
+def nvfp4_scales_from_blocked(blocked, sf, rows, K, stream=None):
+    _check(load().nvfp4_scales_from_blocked(_ptr(blocked), _ptr(sf), rows, K, _stream_handle(stream)))
 
 
 def raw_gemm(A, SFA, B, SFB, C, M, N, K, stream) -> int:

@@ -395,6 +395,115 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
     return flush();
 }
 
+// ---------------------------------------------------------------- blocked scales
+
+nvfp4_status check_scale_matrix(const void *a, const void *b, int rows, int K, const void *blocked)
+{
+    if (rows < 0 || K < 0)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (K % 32 != 0 || K > kMaxK)
+        return NVFP4_ERROR_NOT_SUPPORTED;
+    if (nvfp4::conv_workgroups(rows, K / 16) > 0x7fffffffLL)
+        return NVFP4_ERROR_NOT_SUPPORTED;
+    if (rows == 0 || K == 0)
+        return NVFP4_OK;
+    if (a == nullptr || b == nullptr)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (((uintptr_t)blocked) & 15)
+        return NVFP4_ERROR_INVALID_VALUE; // the blocked side moves in 16-byte pieces
+    return NVFP4_OK;
+}
+
+nvfp4_status convert_one(const void *src, void *dst, int rows, int K, bool to_blocked, hipStream_t stream)
+{
+    nvfp4_status s = check_scale_matrix(src, dst, rows, K, to_blocked ? dst : src);
+    if (s != NVFP4_OK || rows == 0 || K == 0)
+        return s;
+    nvfp4::ScaleConvTable t;
+    memset(&t, 0, sizeof(t));
+    t.count = 1;
+    t.to_blocked = to_blocked ? 1 : 0;
+    t.src[0] = (const uint8_t *)src;
+    t.dst[0] = (uint8_t *)dst;
+    t.rows[0] = rows;
+    t.kb[0] = K / 16;
+    t.prefix[1] = (int)nvfp4::conv_workgroups(rows, K / 16);
+    return nvfp4::launch_scale_conversion(t, stream) == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
+}
+
+// Grouped product with blocked scales: the scales are converted to the plain
+// layout in the stream's workspace (after the tile counters and whatever the
+// plan's K split needs), then the plain path runs on the converted copies.
+nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
+{
+    Plan plan;
+    nvfp4_status s = make_plan(problems, num_groups, &plan);
+    if (s != NVFP4_OK)
+        return s;
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        if (!empty_output(p) && p.K > 0 && ((((uintptr_t)p.SFA) | ((uintptr_t)p.SFB)) & 15))
+            return NVFP4_ERROR_INVALID_VALUE;
+    }
+    if (plan.total_tiles == 0)
+        return NVFP4_OK;
+    auto up = [](long long x) { return (x + 255) & ~255LL; };
+    const long long base = up(std::max<long long>(plan.workspace_bytes, nvfp4::kCounterBytes));
+    std::vector<long long> off_a(num_groups, 0), off_b(num_groups, 0);
+    long long total = base;
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        if (empty_output(p) || p.K == 0)
+            continue;
+        off_a[g] = total;
+        total += up((long long)p.M * (p.K / 16));
+        off_b[g] = total;
+        total += up((long long)p.N * (p.K / 16));
+    }
+    void *ws = nullptr;
+    s = get_workspace((size_t)total, stream, &ws);
+    if (s != NVFP4_OK)
+        return s;
+    std::vector<nvfp4_problem> plain(problems, problems + num_groups);
+    nvfp4::ScaleConvTable t;
+    memset(&t, 0, sizeof(t));
+    auto flush = [&]() -> nvfp4_status {
+        if (t.count == 0)
+            return NVFP4_OK;
+        const hipError_t e = nvfp4::launch_scale_conversion(t, stream);
+        memset(&t, 0, sizeof(t));
+        return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
+    };
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        if (empty_output(p) || p.K == 0)
+            continue;
+        plain[g].SFA = (uint8_t *)ws + off_a[g];
+        plain[g].SFB = (uint8_t *)ws + off_b[g];
+        const void *srcs[2] = {p.SFA, p.SFB};
+        const void *dsts[2] = {plain[g].SFA, plain[g].SFB};
+        const int rows[2] = {p.M, p.N};
+        for (int o = 0; o < 2; ++o) {
+            const long long words = nvfp4::conv_workgroups(rows[o], p.K / 16);
+            if (t.count == nvfp4::kMaxConvEntries || (long long)t.prefix[t.count] + words > 0x7fffffffLL) {
+                s = flush();
+                if (s != NVFP4_OK)
+                    return s;
+            }
+            const int e = t.count++;
+            t.src[e] = (const uint8_t *)srcs[o];
+            t.dst[e] = (uint8_t *)dsts[o];
+            t.rows[e] = rows[o];
+            t.kb[e] = p.K / 16;
+            t.prefix[e + 1] = t.prefix[e] + (int)words;
+        }
+    }
+    s = flush();
+    if (s != NVFP4_OK)
+        return s;
+    return run(plain.data(), num_groups, stream);
+}
+
 } // namespace
 
 extern "C" {
@@ -452,6 +561,43 @@ nvfp4_status nvfp4_group_gemm_plan(const nvfp4_problem *problems, int num_groups
         for (int g = 0; g <= num_groups; ++g)
             tile_prefix[g] = plan.prefix[g];
     return NVFP4_OK;
+}
+
+long long nvfp4_blocked_scale_bytes(int rows, int K)
+{
+    if (rows < 0 || K < 0 || K % 32 != 0 || K > kMaxK)
+        return -1;
+    return (long long)((rows + 127) / 128) * ((K / 16 + 3) / 4) * 512;
+}
+
+nvfp4_status nvfp4_scales_to_blocked(const void *sf, void *blocked, int rows, int K, hipStream_t stream)
+{
+    return convert_one(sf, blocked, rows, K, true, stream);
+}
+
+nvfp4_status nvfp4_scales_from_blocked(const void *blocked, void *sf, int rows, int K, hipStream_t stream)
+{
+    return convert_one(blocked, sf, rows, K, false, stream);
+}
+
+nvfp4_status nvfp4_gemm_blocked(const void *A, const void *SFA, const void *B, const void *SFB, void *C, int M,
+                                int N, int K, hipStream_t stream)
+{
+    nvfp4_problem p;
+    p.A = A;
+    p.SFA = SFA;
+    p.B = B;
+    p.SFB = SFB;
+    p.C = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    return run_blocked(&p, 1, stream);
+}
+
+nvfp4_status nvfp4_group_gemm_blocked(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
+{
+    return run_blocked(problems, num_groups, stream);
 }
 
 nvfp4_status nvfp4_release_workspaces(void)

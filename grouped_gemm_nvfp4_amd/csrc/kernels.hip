@@ -1036,6 +1036,86 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
     }
 }
 
+// ----------------------------------------------------------------------------
+// Scale layout conversion (see ScaleConvTable).  A workgroup of 256 threads
+// takes one 128-row tile and kConvAtoms consecutive atoms (4 KiB): the blocked
+// side moves as coalesced 16-byte lane pieces, the plain side through LDS as
+// 16-byte row pieces (bytes, as plain rows start at any byte).
+__global__ __launch_bounds__(256) void scale_conversion_kernel(ScaleConvTable tab)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t atoms[kConvAtoms * 512];
+    const int wgi = (int)blockIdx.x;
+    int lo = 0, hi = tab.count;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tab.prefix[mid] <= wgi)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int e = lo;
+    const int kb = tab.kb[e], rows = tab.rows[e];
+    const int rest_k = (kb + 3) / 4;
+    const int runs = (rest_k + kConvAtoms - 1) / kConvAtoms;
+    const int local = wgi - tab.prefix[e];
+    const int tm = local / runs, t0 = (local - tm * runs) * kConvAtoms;
+    const int natoms = min(kConvAtoms, rest_k - t0);
+    const int tid = threadIdx.x;
+    // blocked side: thread -> atom tid / 32, 16-byte piece tid % 32
+    const int pa = tid >> 5, pp = tid & 31;
+    const long blk_off = ((long)tm * rest_k + t0 + pa) * 512 + pp * 16;
+    // plain side: thread -> row tid / 2, blocks [16 (tid % 2), +16) of the run
+    const int r = tid >> 1, jh = (tid & 1) * 16;
+    const int m = tm * 128 + r;
+    auto lds_byte = [&](int j) -> uint8_t & { // block j (0..31) of row r in the run
+        return atoms[(j >> 2) * 512 + (r % 32) * 16 + (r / 32) * 4 + (j & 3)];
+    };
+    // the thread's 16 plain bytes as one 16-byte access when they are whole
+    // and 16-byte aligned (K % 256 == 0 and an aligned base), else bytes
+    const uint8_t *plain_in = tab.to_blocked ? tab.src[e] : nullptr;
+    uint8_t *plain_out = tab.to_blocked ? nullptr : tab.dst[e];
+    const long plain_off = (long)m * kb + 4 * t0 + jh;
+    const bool whole = m < rows && 4 * t0 + jh + 16 <= kb &&
+                       (((uintptr_t)(tab.to_blocked ? (const void *)plain_in : (const void *)plain_out) + plain_off) & 15) == 0;
+    if (tab.to_blocked) {
+        if (whole) {
+            const u32x4 v = *(const u32x4 *)(plain_in + plain_off);
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                lds_byte(jh + j) = (uint8_t)(v[j >> 2] >> (8 * (j & 3)));
+        } else {
+            const uint8_t *src = plain_in + (long)m * kb;
+#pragma unroll
+            for (int j = jh; j < jh + 16; ++j) {
+                const int blk = 4 * t0 + j;
+                lds_byte(j) = (m < rows && blk < kb) ? src[blk] : 0;
+            }
+        }
+        __syncthreads();
+        if (pa < natoms)
+            *(u32x4 *)(tab.dst[e] + blk_off) = *(const u32x4 *)(atoms + pa * 512 + pp * 16);
+    } else {
+        if (pa < natoms)
+            *(u32x4 *)(atoms + pa * 512 + pp * 16) = *(const u32x4 *)(tab.src[e] + blk_off);
+        __syncthreads();
+        if (whole) {
+            u32x4 v = (u32x4){0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j >> 2] |= (uint32_t)lds_byte(jh + j) << (8 * (j & 3));
+            *(u32x4 *)(plain_out + plain_off) = v;
+        } else if (m < rows) {
+            uint8_t *dst = plain_out + (long)m * kb;
+#pragma unroll
+            for (int j = jh; j < jh + 16; ++j) {
+                const int blk = 4 * t0 + j;
+                if (blk < kb)
+                    dst[blk] = lds_byte(j);
+            }
+        }
+    }
+}
+
 } // namespace
 
 hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, int sk_workgroups,
@@ -1088,6 +1168,15 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
     }
     }
+}
+
+hipError_t launch_scale_conversion(const ScaleConvTable &table, hipStream_t stream)
+{
+    const int wgs = table.prefix[table.count];
+    if (wgs <= 0)
+        return hipSuccess;
+    void *args[] = {const_cast<ScaleConvTable *>(&table)};
+    return hipLaunchKernel((const void *)scale_conversion_kernel, dim3((unsigned)wgs), dim3(256), args, 0, stream);
 }
 
 } // namespace nvfp4

@@ -89,4 +89,33 @@ inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_
 hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, int sk_workgroups,
                           hipStream_t stream);
 
+// Scale-layout conversion, batched: entry e moves the scales of a
+// rows[e] x (kb[e] = K/16) matrix between the plain [rows][K/16] layout and
+// the blocked one (512-byte atoms of 128 rows x 4 blocks; byte of row m,
+// block j at ((m / 128) * ceil(kb / 4) + j / 4) * 512 + (m % 32) * 16 +
+// ((m / 32) % 4) * 4 + j % 4; padding rows and blocks are zero).  One
+// workgroup per 128-row tile and run of kConvAtoms atoms; prefix[e] =
+// workgroups of the entries before e.
+constexpr int kMaxConvEntries = 128;
+constexpr int kConvAtoms = 8;
+struct ScaleConvTable {
+    int count;
+    int to_blocked; // 1: plain -> blocked (padding written as zero); 0: blocked -> plain
+    int prefix[kMaxConvEntries + 1];
+    const uint8_t *src[kMaxConvEntries];
+    uint8_t *dst[kMaxConvEntries];
+    int rows[kMaxConvEntries];
+    int kb[kMaxConvEntries];
+};
+static_assert(sizeof(ScaleConvTable) <= 4096, "kernel-argument budget");
+
+// Workgroups of one entry.
+inline long long conv_workgroups(int rows, int kb)
+{
+    const long long rest_k = (kb + 3) / 4;
+    return (rows + 127LL) / 128 * ((rest_k + kConvAtoms - 1) / kConvAtoms);
+}
+
+hipError_t launch_scale_conversion(const ScaleConvTable &table, hipStream_t stream);
+
 } // namespace nvfp4

@@ -96,6 +96,45 @@ nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const voi
 nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups,
                               hipStream_t stream);
 
+/* ---- Blocked scale layout: the layout the kernelbot pages' kernels consume
+ * (raw-CUDA page nvfp4-group-gemm-407526, device kernel, scale TMA issue: a
+ * 128-row tile's scales start at (tile * K/64) * 512 bytes and advance 2048
+ * bytes per 256 K; single-GEMM page nvfp4-gemm-125598, `custom_kernel`
+ * docstring: permuted scales of shape [32, 4, rest_m, 4, rest_k, l]).
+ *
+ * 512-byte atoms, each holding the scales of 128 rows x 4 consecutive K/16
+ * blocks; atom (row tile tm, K atom ka) at byte (tm * ceil(K/64) + ka) * 512;
+ * inside it, row r (0..127) block c (0..3) at (r % 32) * 16 + (r / 32) * 4 +
+ * c.  Rows pad to a multiple of 128 and blocks to a multiple of 4, with zero
+ * bytes. */
+
+/* Bytes of the blocked layout of a rows x K/16 scale matrix; -1 if rows < 0,
+ * K < 0, K % 32 != 0 or K > 2^24. */
+long long nvfp4_blocked_scale_bytes(int rows, int K);
+
+/* Plain [rows][K/16] -> blocked (every byte of the blocked buffer is written,
+ * padding as zero), and blocked -> plain.  Device pointers, the blocked one
+ * 16-byte aligned; asynchronous on `stream`; rows == 0 or K == 0 does nothing.
+ * Errors: INVALID_VALUE for negative sizes, NULL pointers (when there is
+ * something to move) or a misaligned blocked pointer; NOT_SUPPORTED for
+ * K % 32 != 0 or K > 2^24; LAUNCH if the kernel launch fails. */
+nvfp4_status nvfp4_scales_to_blocked(const void *sf, void *blocked, int rows, int K,
+                                     hipStream_t stream);
+nvfp4_status nvfp4_scales_from_blocked(const void *blocked, void *sf, int rows, int K,
+                                       hipStream_t stream);
+
+/* nvfp4_gemm / nvfp4_group_gemm with SFA and SFB in the blocked layout
+ * (16-byte aligned, nvfp4_blocked_scale_bytes(M or N, K) bytes each).  The
+ * scales are first converted to the plain layout inside the library's
+ * per-stream device workspace (so the call may allocate it, and returns
+ * NOT_SUPPORTED inside a stream capture if it would have to); then the plain
+ * path runs, so C is bitwise what nvfp4_gemm gives for the same scales.
+ * Other arguments, limits and errors as for the plain entry points. */
+nvfp4_status nvfp4_gemm_blocked(const void *A, const void *SFA, const void *B, const void *SFB,
+                                void *C, int M, int N, int K, hipStream_t stream);
+nvfp4_status nvfp4_group_gemm_blocked(const nvfp4_problem *problems, int num_groups,
+                                      hipStream_t stream);
+
 /* How a call would be carried out (host only, no HIP call).  For tests and
  * reports. */
 typedef struct {

@@ -133,3 +133,48 @@ def test_problem_struct_matches_header_layout():
     # 5 pointers then 3 ints, natural alignment
     assert ctypes.sizeof(b.Nvfp4Problem) == 5 * 8 + 3 * 4 + 4
     assert b.Nvfp4Problem.M.offset == 40
+
+
+# ------------------------------------------------------------ blocked scale layout
+
+@pytest.mark.parametrize("rows,K", [(0, 64), (1, 32), (128, 256), (129, 96), (300, 7168), (5, 0)])
+def test_blocked_scale_bytes_match_the_layout(rows, K):
+    import oracle
+    assert b.nvfp4_blocked_scale_bytes(rows, K) == oracle.blocked_scale_shape(rows, K)[2]
+
+
+@pytest.mark.parametrize("rows,K", [(-1, 32), (4, -32), (4, 48), (4, (1 << 24) + 32)])
+def test_blocked_scale_bytes_reject_bad_sizes(rows, K):
+    assert b.nvfp4_blocked_scale_bytes(rows, K) == -1
+
+
+@pytest.mark.parametrize("fn", ["nvfp4_scales_to_blocked", "nvfp4_scales_from_blocked"])
+def test_scale_conversion_rejects_bad_arguments(fn):
+    f = getattr(g.load(), fn)
+    assert f(ALIGNED, ALIGNED, -1, 64, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, ALIGNED, 4, 48, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    assert f(None, ALIGNED, 4, 64, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, None, 4, 64, None) == b.NVFP4_ERROR_INVALID_VALUE
+    # the blocked side moves in 16-byte pieces: it must be 16-byte aligned
+    for off in (2, 4, 8):
+        if fn == "nvfp4_scales_to_blocked":
+            assert f(ALIGNED, ALIGNED + off, 4, 64, None) == b.NVFP4_ERROR_INVALID_VALUE
+        else:
+            assert f(ALIGNED + off, ALIGNED, 4, 64, None) == b.NVFP4_ERROR_INVALID_VALUE
+    # nothing to move: no launch, no pointer needed
+    assert f(None, None, 0, 64, None) == b.NVFP4_OK
+    assert f(None, None, 7, 0, None) == b.NVFP4_OK
+
+
+def test_blocked_gemm_rejects_bad_arguments():
+    lib = g.load()
+    assert lib.nvfp4_gemm_blocked(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 48, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+    assert lib.nvfp4_gemm_blocked(ALIGNED, None, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64, None) == \
+        b.NVFP4_ERROR_INVALID_VALUE
+    assert lib.nvfp4_gemm_blocked(ALIGNED, ALIGNED + 1, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64, None) == \
+        b.NVFP4_ERROR_INVALID_VALUE
+    assert lib.nvfp4_gemm_blocked(ALIGNED, ALIGNED, ALIGNED, ALIGNED + 8, ALIGNED, 8, 8, 64, None) == \
+        b.NVFP4_ERROR_INVALID_VALUE
+    assert lib.nvfp4_gemm_blocked(None, None, None, None, None, 0, 8, 64, None) == b.NVFP4_OK
+    assert lib.nvfp4_group_gemm_blocked(None, 0, None) == b.NVFP4_OK

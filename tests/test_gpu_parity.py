@@ -358,3 +358,70 @@ def test_grouped_workload_reduced_full_compare(lib):
     for gi, (p, got) in enumerate(zip(probs, outs)):
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "moe-reduced group %d" % gi)
+
+
+# ------------------------------------------------------------ blocked scale layout
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (128, 256), (300, 96), (129, 1056), (512, 7168)])
+def test_scales_to_blocked_matches_oracle(lib, rows, K):
+    """Every byte of the blocked buffer, padding included, as the oracle's
+    layout (the buffer is poisoned first)."""
+    rng = np.random.default_rng(rows * 7 + K)
+    sf = rng.integers(0, 256, (rows, K // 16), dtype=np.uint8)
+    nbytes = lib.nvfp4_blocked_scale_bytes(rows, K)
+    blk = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    lib.nvfp4_scales_to_blocked(to_dev(sf), blk, rows, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(blk.cpu().numpy(), oracle.scales_to_blocked(sf, rows, K))
+    back = torch.full((rows, K // 16), 0xCD, dtype=torch.uint8, device="cuda")
+    lib.nvfp4_scales_from_blocked(blk, back, rows, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), sf)
+
+
+def blocked_dev(sf, rows, K):
+    return to_dev(oracle.scales_to_blocked(sf, rows, K))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 6144, 8192),    # panel kernel with a K split (tile counters in the workspace)
+    (40, 500, 1024),     # stream kernel
+    (300, 260, 2080),    # tiled kernel, ragged K tile
+])
+def test_gemm_blocked_equals_plain(lib, M, N, K):
+    p = inputs.draw_problems(5400 + M + K, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    plain = bits(C)
+    C2 = poisoned(M, N)
+    lib.nvfp4_gemm_blocked(A, blocked_dev(p.SFA, M, K), B, blocked_dev(p.SFB, N, K), C2, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(C2), plain)
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(plain, c16, bound, "blocked %dx%dx%d" % (M, N, K))
+
+
+def test_group_gemm_blocked_then_plain_split(lib):
+    """A grouped call with blocked scales, then a plain call that splits K on
+    the same stream: the converted scales live past the tile counters, so the
+    second call's counters still start at zero."""
+    shapes = [(200, 300, 1536), (64, 257, 512), (0, 64, 256), (130, 70, 0)]
+    probs = inputs.draw_problems(41, shapes)
+    devs = [dev_problem(p) for p in probs]
+    lib.nvfp4_group_gemm_blocked([(d[0], blocked_dev(p.SFA, p.M, p.K) if p.K else d[1], d[2],
+                                   blocked_dev(p.SFB, p.N, p.K) if p.K else d[3], d[4], p.M, p.N, p.K)
+                                  for d, p in zip(devs, probs)])
+    torch.cuda.synchronize()
+    for i, (d, p) in enumerate(zip(devs, probs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        got = bits(d[4])
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "blocked group %d" % i)
+    (q,) = inputs.draw_problems(42, [(64, 64, 16384)])
+    assert lib.gemm_plan(64, 64, 16384)["split_k"] > 1
+    check_full(lib, q, "split after blocked")
