@@ -1037,6 +1037,200 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 }
 
 // ----------------------------------------------------------------------------
+// One-wave 128 x 128 tile kernel with direct global -> LDS loads (gfx950
+// buffer_load ... lds, 16 bytes per lane for A and B, 4 for the scales): no
+// register staging slot, so the registers it would hold go to the compute.
+// Two LDS stages as separate arrays (the compiler then waits only for the
+// stage it reads): tile kt + 1 streams into one while tile kt is computed
+// from the other.  The 16-byte chunk swizzle of the register-staged kernel is
+// kept by choosing each lane's global chunk: a load instruction fills 16
+// rows of 64 bytes, lane i landing at row i / 4, physical chunk i % 4, so it
+// fetches logical chunk (i % 4) ^ ((row / 4) % 4).  Vector path only (K % 128
+// == 0, 8-byte aligned scales).
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
+{
+    using namespace tiled;
+    __shared__ __attribute__((aligned(16))) uint8_t stages[2 * kStageBytes];
+    uint8_t *const stage0 = stages;
+    uint8_t *const stage1 = stages + kStageBytes;
+
+    const int w = blockIdx.x;
+    const int gi = find_group(tab, w);
+    const GemmDesc &d = tab.g[gi];
+    const int r = w - tab.prefix[gi];
+    const int tm = r % d.tiles_m;
+    const int tn = r / d.tiles_m;
+    const int M = d.M, N = d.N, K = d.K;
+    const int row0 = tm * BM, col0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const uint32_t sh = h * 16;
+
+    const int kb_row = K / 2;
+    const int ks_row = K / 16;
+    const int nkt = K / BK;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
+
+    // data: instruction j covers rows 16 j .. 16 j + 15
+    const int drow = lane >> 2;
+    const uint32_t d_off = (uint32_t)(drow * kb_row + (((lane & 3) ^ ((drow >> 2) & 3)) << 4));
+    // scales: instruction j covers rows 32 j .. 32 j + 31 (two dwords each)
+    const uint32_t s_off = (uint32_t)((lane >> 1) * ks_row + (lane & 1) * 4);
+
+    // tile kt into stage `st` (tiles past nkt read as zero)
+    auto issue = [&](uint8_t *st, int kt) {
+        const bool live = kt < nkt;
+        const uint32_t kb = (uint32_t)kt * kRowBytes, ks = (uint32_t)kt * kSfBytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = live ? d_off + (uint32_t)(16 * j * kb_row) + kb : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(st + kAOff + 1024 * j), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(st + kBOff + 1024 * j), 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t off = live ? s_off + (uint32_t)(32 * j * ks_row) + ks : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff + 256 * j), 4, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff + 256 * j), 4, off, 0, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = (f32x16){};
+
+    // MFMA work of the 128-K tile in stage st: two 64-K groups g.  Issue
+    // order (scheduling groups): the LDS reads, the scale conversion and
+    // first decode step, then every MFMA followed by the next step's decode
+    // VALU (4 per MFMA, 5 across the group boundary, where the second
+    // group's scales and first step are decoded), then the last step's MFMAs.
+    auto compute = [&](const uint8_t *st) {
+        half2_t ca[2][4], cb[2][4];
+        u32x4 pa[2][4], pb[2][4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
+                const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
+                ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
+                cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
+                pa[g][i] = *(const u32x4 *)(st + kAOff + swz(32 * i + l32, 2 * g + h));
+                pb[g][i] = *(const u32x4 *)(st + kBOff + swz(32 * i + l32, 2 * g + h));
+            }
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                half8_t fa[4], fb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    fa[i] = decode8(pa[g][i][q], q < 2 ? bcast_lo(ca[g][i]) : bcast_hi(ca[g][i]));
+                    fb[i] = decode8(pb[g][i][q], q < 2 ? bcast_lo(cb[g][i]) : bcast_hi(cb[g][i]));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+#ifndef NVFP4_NO_SCHED_GROUPS
+        __builtin_amdgcn_sched_group_barrier(0x100, 32, 0); // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 80, 0); // group 0 scales + step 0 decode
+#pragma unroll
+        for (int k = 0; k < 48; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) { // group 1 scales + step 0 under group 0's last MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 48; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+#endif
+    };
+
+    // The compiler does not order these loads' LDS writes before the reads
+    // of the same array, so the waits are explicit: before a stage is read,
+    // at most the other stage's kIssued loads may still be in flight
+    // (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
+    // lgkmcnt 11:8 left at their maxima).
+    constexpr int kIssued = 8 + 8 + 4 + 4;
+    constexpr int kWaitOther = ((kIssued >> 4) << 14) | (15 << 8) | (7 << 4) | (kIssued & 15);
+    if (nkt > 0) {
+        issue(stage0, 0);
+        for (int kt = 0; kt < nkt; kt += 2) {
+            issue(stage1, kt + 1);
+            SCHED_FENCE();
+            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage0 has landed
+            SCHED_FENCE();
+            compute(stage0);
+            SCHED_FENCE();
+            issue(stage0, kt + 2);
+            SCHED_FENCE();
+            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage1 has landed
+            SCHED_FENCE();
+            // with an odd tile count the last stage1 tile is out of range:
+            // zeros, adding exact zeros (no branch around the accumulators)
+            compute(stage1);
+            SCHED_FENCE();
+        }
+    }
+
+    // epilogue: fp16 (round to nearest even) rows 0..63 into stage0 and rows
+    // 64..127 into stage1 (the loop's last reads are done: each wave reads
+    // only what it wrote), then 16-byte row-contiguous stores masked to M x N
+    // (the tile's trailing zero-tile loads were out of range: nothing lands)
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
+                const int col = 32 * j + l32;
+                uint8_t *sC = row < 64 ? stage0 : stage1;
+                *(uint16_t *)(sC + (row & 63) * kCStride + col * 2) = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
+            }
+    const bool vec_ok = (N % 8 == 0) && ((((uintptr_t)d.C) & 15) == 0);
+#pragma unroll 4
+    for (int s2 = 0; s2 < BM * BN / 8 / 64; ++s2) {
+        const int seg = s2 * 64 + lane;
+        const int row = seg >> 4, c8 = (seg & 15) * 8;
+        const int grow = row0 + row, gcol = col0 + c8;
+        if (grow >= M)
+            continue;
+        const uint8_t *sC = row < 64 ? stage0 : stage1;
+        uint16_t *dst = d.C + (long)grow * N + gcol;
+        const uint16_t *src = (const uint16_t *)(sC + (row & 63) * kCStride + c8 * 2);
+        if (vec_ok && gcol + 8 <= N) {
+            *(u32x4 *)dst = *(const u32x4 *)src;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gcol + e < N)
+                    dst[e] = src[e];
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
 // Scale layout conversion (see ScaleConvTable).  A workgroup of 256 threads
 // takes one 128-row tile and kConvAtoms consecutive atoms (4 KiB): the blocked
 // side moves as coalesced 16-byte lane pieces, the plain side through LDS as
@@ -1163,6 +1357,12 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             return hipLaunchKernel(fn, dim3(sk_workgroups), dim3(64), args, 0, stream);
         }
         const bool four = cfg == kTile128x128K4;
+#ifndef NVFP4_TILED_NO_DMA
+        if (!four && vec) {
+            void *dargs[] = {const_cast<GroupTable *>(&table)};
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel, dim3(tiles), dim3(64), dargs, 0, stream);
+        }
+#endif
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4, false> : (const void *)gemm_tiled_kernel<false, 4, false>)
                               : (vec ? (const void *)gemm_tiled_kernel<true, 1, false> : (const void *)gemm_tiled_kernel<false, 1, false>);
         return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
