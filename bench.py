@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--scale-layout", choices=("plain", "blocked"), default="plain",
                     help="scales as [rows][K/16] (default) or in the pages' blocked 512-byte atoms "
                          "(nvfp4_gemm_blocked / nvfp4_group_gemm_blocked)")
+    ap.add_argument("--scales", choices=("general", "pow2"), default="general",
+                    help="scales uniform over the 49 e4m3 codes in [0.125, 8] (default), or over their "
+                         "seven powers of two, run on the FP4-MFMA path (nvfp4_gemm_pow2scale / "
+                         "nvfp4_group_gemm_pow2scale)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     return ap.parse_args()
@@ -163,7 +167,11 @@ def main():
 
     lib = g.load()
     wl = inputs.WORKLOADS[args.workload]
-    probs = inputs.draw_workload(args.workload)
+    pow2 = args.scales == "pow2"
+    if pow2 and args.scale_layout != "plain":
+        print("--scales pow2 takes plain-layout scales only", file=sys.stderr)
+        sys.exit(2)
+    probs = inputs.draw_workload(args.workload, inputs.POW2_SCALE_CODES if pow2 else inputs.SCALE_CODES)
     shapes = [(p.M, p.N, p.K) for p in probs]
     flops = inputs.flops(shapes)
     alg_bytes = inputs.algorithmic_bytes(shapes)
@@ -214,8 +222,9 @@ def main():
                 arr[i] = b.Nvfp4Problem(A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
                                         SFB.data_ptr(), C.data_ptr(), p.M, p.N, p.K)
             calls.append(("group", (arr, len(one), sh)))
-    gemm_fn = lib.nvfp4_gemm_blocked if blocked else lib.nvfp4_gemm
-    group_fn = lib.nvfp4_group_gemm_blocked if blocked else lib.nvfp4_group_gemm
+    gemm_fn = lib.nvfp4_gemm_blocked if blocked else lib.nvfp4_gemm_pow2scale if pow2 else lib.nvfp4_gemm
+    group_fn = (lib.nvfp4_group_gemm_blocked if blocked else
+                lib.nvfp4_group_gemm_pow2scale if pow2 else lib.nvfp4_group_gemm)
 
     def step(i):
         kind, a = calls[i % len(calls)]
@@ -277,6 +286,10 @@ def main():
         roof = {"bound": "hbm", "achieved": kern_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": kern_gbps / PEAK_HBM_GBPS,
                 "traffic": None if blocked else measured_traffic(wl.name)}
+    elif pow2:
+        # the FP4-MFMA path: its own dtype's peak (fp4 x fp4 MFMA)
+        roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP4_TFLOPS,
+                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP4_TFLOPS, "traffic": None}
     else:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS,
@@ -301,11 +314,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "e2m1" if pow2 else "f16",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
                    "shapes_MNK": shapes, "seed": 1000 + args.workload,
-                   "operand_copies": copies, "scale_layout": args.scale_layout},
+                   "operand_copies": copies, "scale_layout": args.scale_layout,
+                   "scales": args.scales},
         "roofline": roof,
         "cpu_baseline": cpu,
         "pct_fp4_peak": 100.0 * kern_tflops / PEAK_FP4_TFLOPS,

@@ -12,8 +12,10 @@ from ._binding import (  # noqa: F401
     nvfp4_blocked_scale_bytes,
     nvfp4_gemm,
     nvfp4_gemm_blocked,
+    nvfp4_gemm_pow2scale,
     nvfp4_group_gemm,
     nvfp4_group_gemm_blocked,
+    nvfp4_group_gemm_pow2scale,
     nvfp4_scales_from_blocked,
     nvfp4_scales_to_blocked,
     release_workspaces,

@@ -23,6 +23,7 @@ EXPORTED = [
     "nvfp4_release_workspaces", "nvfp4_status_string", "nvfp4_abi_version",
     "nvfp4_blocked_scale_bytes", "nvfp4_scales_to_blocked", "nvfp4_scales_from_blocked",
     "nvfp4_gemm_blocked", "nvfp4_group_gemm_blocked",
+    "nvfp4_gemm_pow2scale", "nvfp4_group_gemm_pow2scale",
 ]
 
 
@@ -89,6 +90,10 @@ def load():
     lib.nvfp4_gemm_blocked.restype = ci
     lib.nvfp4_group_gemm_blocked.argtypes = [ctypes.POINTER(Nvfp4Problem), ci, vp]
     lib.nvfp4_group_gemm_blocked.restype = ci
+    lib.nvfp4_gemm_pow2scale.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.nvfp4_gemm_pow2scale.restype = ci
+    lib.nvfp4_group_gemm_pow2scale.argtypes = [ctypes.POINTER(Nvfp4Problem), ci, vp]
+    lib.nvfp4_group_gemm_pow2scale.restype = ci
     _lib = lib
     return lib
 
@@ -163,6 +168,22 @@ def nvfp4_group_gemm_blocked(problems, stream=None):
     for i, (A, SFA, B, SFB, C, M, N, K) in enumerate(problems):
         arr[i] = _problem(A, SFA, B, SFB, C, M, N, K)
     _check(load().nvfp4_group_gemm_blocked(arr, len(problems), _stream_handle(stream)))
+
+
+def nvfp4_gemm_pow2scale(A, SFA, B, SFB, C, M, N, K, stream=None):
+    """nvfp4_gemm for scales that are all powers of two (E4M3 codes with a
+    zero mantissa and a nonzero exponent field), on the scaled FP4 MFMA."""
+    _check(load().nvfp4_gemm_pow2scale(_ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _ptr(C),
+                                       M, N, K, _stream_handle(stream)))
+
+
+def nvfp4_group_gemm_pow2scale(problems, stream=None):
+    """nvfp4_group_gemm for power-of-two scales; ``problems`` as for
+    nvfp4_group_gemm with explicit (A, SFA, B, SFB, C, M, N, K)."""
+    arr = (Nvfp4Problem * max(1, len(problems)))()
+    for i, (A, SFA, B, SFB, C, M, N, K) in enumerate(problems):
+        arr[i] = _problem(A, SFA, B, SFB, C, M, N, K)
+    _check(load().nvfp4_group_gemm_pow2scale(arr, len(problems), _stream_handle(stream)))
 
 
 def nvfp4_blocked_scale_bytes(rows, K) -> int:

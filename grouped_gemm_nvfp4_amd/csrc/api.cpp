@@ -231,7 +231,9 @@ long long stream_k_makespan(const nvfp4_problem *problems, const Plan &plan, con
     return 4 * (per_wg + kFixupUnits + (contributors + 1) / 2);
 }
 
-nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan)
+// pow2: the power-of-two-scale path (one-wave 128 x 128 tiles on the scaled
+// FP4 MFMA, no K split), which needs K % 128 == 0 and 8-byte aligned scales.
+nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan, bool pow2 = false)
 {
     if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS)
         return NVFP4_ERROR_INVALID_VALUE;
@@ -251,6 +253,28 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     int max_ktiles = 0;
     nvfp4_status s = NVFP4_OK;
     plan->split_k = 1;
+    if (pow2) {
+        for (int g = 0; g < num_groups; ++g) {
+            const nvfp4_problem &p = problems[g];
+            if (!empty_output(p) && (p.K % 128 != 0 || ((((uintptr_t)p.SFA) | ((uintptr_t)p.SFB)) & 7) != 0))
+                return NVFP4_ERROR_NOT_SUPPORTED;
+        }
+        plan->cfg = nvfp4::kTile128x128Pow2;
+        s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
+        if (s != NVFP4_OK)
+            return s;
+        const nvfp4::TileShape ts = nvfp4::tile_shape(plan->cfg);
+        plan->tile_m = ts.tile_m;
+        plan->tile_n = ts.tile_n;
+        plan->total_tiles = total;
+        plan->order.resize(num_groups);
+        std::iota(plan->order.begin(), plan->order.end(), 0);
+        std::stable_sort(plan->order.begin(), plan->order.end(), [&](int a, int b) {
+            return problems[a].K > problems[b].K;
+        });
+        plan->workspace_bytes = 0;
+        return NVFP4_OK;
+    }
     if (max_m > 0 && max_m <= 64) {
         // panel: each wave takes at least one 256-K tile of a slice (8 waves)
         plan->cfg = nvfp4::kPanel64x64;
@@ -342,10 +366,10 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
     info->workspace_bytes = plan.workspace_bytes;
 }
 
-nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
+nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream, bool pow2 = false)
 {
     Plan plan;
-    nvfp4_status s = make_plan(problems, num_groups, &plan);
+    nvfp4_status s = make_plan(problems, num_groups, &plan, pow2);
     if (s != NVFP4_OK || plan.total_tiles == 0)
         return s;
 
@@ -526,6 +550,26 @@ nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const voi
 nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
 {
     return run(problems, num_groups, stream);
+}
+
+nvfp4_status nvfp4_gemm_pow2scale(const void *A, const void *SFA, const void *B, const void *SFB, void *C, int M,
+                                  int N, int K, hipStream_t stream)
+{
+    nvfp4_problem p;
+    p.A = A;
+    p.SFA = SFA;
+    p.B = B;
+    p.SFB = SFB;
+    p.C = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    return run(&p, 1, stream, true);
+}
+
+nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
+{
+    return run(problems, num_groups, stream, true);
 }
 
 nvfp4_status nvfp4_gemm_plan(int M, int N, int K, nvfp4_plan_info *info)

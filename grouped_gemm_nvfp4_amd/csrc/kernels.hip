@@ -1040,15 +1040,41 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 // One-wave 128 x 128 tile kernel with direct global -> LDS loads (gfx950
 // buffer_load ... lds, 16 bytes per lane for A and B, 4 for the scales): no
 // register staging slot, so the registers it would hold go to the compute.
-// Two LDS stages as separate arrays (the compiler then waits only for the
-// stage it reads): tile kt + 1 streams into one while tile kt is computed
-// from the other.  The 16-byte chunk swizzle of the register-staged kernel is
-// kept by choosing each lane's global chunk: a load instruction fills 16
-// rows of 64 bytes, lane i landing at row i / 4, physical chunk i % 4, so it
-// fetches logical chunk (i % 4) ^ ((row / 4) % 4).  Vector path only (K % 128
-// == 0, 8-byte aligned scales).
+// Two LDS stages in one array: tile kt + 1 streams into one while tile kt is
+// computed from the other, with explicit waits (below).  The 16-byte chunk
+// swizzle of the register-staged kernel is kept by choosing each lane's
+// global chunk: a load instruction fills 16 rows of 64 bytes, lane i landing
+// at row i / 4, physical chunk i % 4, so it fetches logical chunk (i % 4) ^
+// ((row / 4) % 4).  Vector path only (K % 128 == 0, 8-byte aligned scales).
+//
+// kPow2: every scale is a power of two, E4M3 codes with a zero mantissa and
+// exponent field e in 1..15 (2^-6 .. 2^8).  Then a s_a b s_b = (a b) 2^(ea +
+// eb), so the packed codes go to the scaled FP4 MFMA (v_mfma_scale_f32_
+// 32x32x64_f8f6f4) undecoded, with the scales as E8M0 exponents (e + 120).
+// That MFMA applies one scale per lane to 32 K slots; NVFP4 scales cover 16,
+// so each lane's 32 slots hold one 16-value block and 16 zeros: a step of
+// four lanes-halves covers blocks 2 s (lanes 0-31) and 2 s + 1 (lanes 32-63)
+// of every row, 32 real K per 32x32 MFMA (the fp16 path needs two MFMAs and
+// eight decode instructions per fragment for the same 32 K).  Other scale
+// codes are outside this path's contract (their mantissa bits are ignored).
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// The 16 MFMAs of one power-of-two step: the scale bytes sit in byte kSel of
+// each lane's exponent dwords.
+template <int kSel>
+__device__ inline void mfma_pow2_step(f32x16 (&acc)[4][4], const i32x8 (&fa)[4], const i32x8 (&fb)[4],
+                                      const uint32_t (&ea)[4], const uint32_t (&eb)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4, kSel,
+                                                                         (int)ea[i], kSel, (int)eb[j]);
+}
+
+template <bool kPow2>
 __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
 {
     using namespace tiled;
@@ -1165,6 +1191,40 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
 #endif
     };
 
+    // power-of-two scales: step s (blocks 2 s + h of every row) of the 128-K
+    // tile in stage st on the scaled FP4 MFMA
+    auto compute_pow2 = [&](const uint8_t *st) {
+        // E8M0 exponents of the lane's rows: dword d holds blocks 4 d + h ..
+        // (shifted down by h bytes), so block 2 s + h sits in byte 2 (s % 2)
+        // of dword s / 2
+        uint32_t ea[2][4], eb[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
+            const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                ea[d][i] = ((va[d] >> (8 * h + 3)) & 0x0F0F0F0Fu) + 0x78787878u;
+                eb[d][i] = ((vb[d] >> (8 * h + 3)) & 0x0F0F0F0Fu) + 0x78787878u;
+            }
+        }
+#pragma unroll
+        for (int st4 = 0; st4 < 4; ++st4) {
+            i32x8 fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 xa = *(const u32x2 *)(st + kAOff + swz(32 * i + l32, st4) + 8 * h);
+                const u32x2 xb = *(const u32x2 *)(st + kBOff + swz(32 * i + l32, st4) + 8 * h);
+                fa[i] = (i32x8){(int)xa.x, (int)xa.y, 0, 0, 0, 0, 0, 0};
+                fb[i] = (i32x8){(int)xb.x, (int)xb.y, 0, 0, 0, 0, 0, 0};
+            }
+            if (st4 & 1)
+                mfma_pow2_step<2>(acc, fa, fb, ea[st4 >> 1], eb[st4 >> 1]);
+            else
+                mfma_pow2_step<0>(acc, fa, fb, ea[st4 >> 1], eb[st4 >> 1]);
+        }
+    };
+
     // The compiler does not order these loads' LDS writes before the reads
     // of the same array, so the waits are explicit: before a stage is read,
     // at most the other stage's kIssued loads may still be in flight
@@ -1179,7 +1239,10 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
             SCHED_FENCE();
             __builtin_amdgcn_s_waitcnt(kWaitOther); // stage0 has landed
             SCHED_FENCE();
-            compute(stage0);
+            if (kPow2)
+                compute_pow2(stage0);
+            else
+                compute(stage0);
             SCHED_FENCE();
             issue(stage0, kt + 2);
             SCHED_FENCE();
@@ -1187,7 +1250,10 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
             SCHED_FENCE();
             // with an odd tile count the last stage1 tile is out of range:
             // zeros, adding exact zeros (no branch around the accumulators)
-            compute(stage1);
+            if (kPow2)
+                compute_pow2(stage1);
+            else
+                compute(stage1);
             SCHED_FENCE();
         }
     }
@@ -1344,6 +1410,7 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
     }
     case kTile128x128K4:
     case kTile128x128SK:
+    case kTile128x128Pow2:
     case kTile128x128:
     default: {
         bool vec = true;
@@ -1357,10 +1424,16 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             return hipLaunchKernel(fn, dim3(sk_workgroups), dim3(64), args, 0, stream);
         }
         const bool four = cfg == kTile128x128K4;
+        if (cfg == kTile128x128Pow2) {
+            if (!vec)
+                return hipErrorInvalidValue;
+            void *dargs[] = {const_cast<GroupTable *>(&table)};
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true>, dim3(tiles), dim3(64), dargs, 0, stream);
+        }
 #ifndef NVFP4_TILED_NO_DMA
         if (!four && vec) {
             void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel, dim3(tiles), dim3(64), dargs, 0, stream);
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
 #endif
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4, false> : (const void *)gemm_tiled_kernel<false, 4, false>)

@@ -28,6 +28,8 @@ import numpy as np
 
 # The 49 finite positive e4m3fn codes with values in [0.125, 8].
 SCALE_CODES = np.arange(0x20, 0x51, dtype=np.uint8)
+# Their powers of two (zero mantissa): 0.125, 0.25, ..., 8.
+POW2_SCALE_CODES = np.arange(0x20, 0x51, 8, dtype=np.uint8)
 GROUP_M_CHOICES = np.arange(64, 513, 64)
 
 
@@ -59,10 +61,11 @@ def draw_problem(rng: np.random.Generator, M: int, N: int, K: int,
     return Problem(M, N, K, A, SFA, B, SFB)
 
 
-def draw_problems(seed: int, shapes) -> List[Problem]:
-    """Problems for a list of (M, N, K) shapes, drawn from one seeded stream."""
+def draw_problems(seed: int, shapes, scale_codes: np.ndarray = SCALE_CODES) -> List[Problem]:
+    """Problems for a list of (M, N, K) shapes, drawn from one seeded stream
+    (scales uniform over ``scale_codes``)."""
     rng = np.random.default_rng(seed)
-    return [draw_problem(rng, M, N, K) for (M, N, K) in shapes]
+    return [draw_problem(rng, M, N, K, scale_codes) for (M, N, K) in shapes]
 
 
 @dataclass(frozen=True)
@@ -103,8 +106,9 @@ def workload_shapes(index: int):
     raise IndexError(index)
 
 
-def draw_workload(index: int) -> List[Problem]:
-    """All problems of the named workload ``index`` (see ``WORKLOADS``).
+def draw_workload(index: int, scale_codes: np.ndarray = SCALE_CODES) -> List[Problem]:
+    """All problems of the named workload ``index`` (see ``WORKLOADS``), with
+    scales uniform over ``scale_codes``.
 
     The 8-group workload's per-group M comes from the same seeded stream,
     drawn before the operands."""
@@ -112,7 +116,7 @@ def draw_workload(index: int) -> List[Problem]:
     rng = np.random.default_rng(seed)
     if index == 3:
         rng.choice(GROUP_M_CHOICES, size=8)  # advance past the M draw
-    return [draw_problem(rng, M, N, K) for (M, N, K) in shapes]
+    return [draw_problem(rng, M, N, K, scale_codes) for (M, N, K) in shapes]
 
 
 def flops(shapes) -> int:

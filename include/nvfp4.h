@@ -135,6 +135,30 @@ nvfp4_status nvfp4_gemm_blocked(const void *A, const void *SFA, const void *B, c
 nvfp4_status nvfp4_group_gemm_blocked(const nvfp4_problem *problems, int num_groups,
                                       hipStream_t stream);
 
+/* ---- Power-of-two scales on the scaled FP4 MFMA.  Not a kernel of the
+ * kernelbot pages: a special case of their operation (the grouped page
+ * nvfp4-group-gemm-498453 and the single-GEMM page nvfp4-gemm-125598,
+ * `custom_kernel`: C = A * SFA * B * SFB, sf_vec_size 16) for inputs whose
+ * scales are all powers of two, which lets the packed e2m1 codes feed gfx950's
+ * v_mfma_scale_f32_32x32x64_f8f6f4 without decoding (each scale becomes an
+ * E8M0 exponent; each 16-value block rides in 32 MFMA K slots with 16 zeros).
+ *
+ * Same arguments, layouts, asynchrony and results as nvfp4_gemm /
+ * nvfp4_group_gemm (fp32 accumulation, fp16 round-to-nearest-even), for
+ * inputs whose every SFA and SFB code is a positive normal power of two:
+ * e4m3fn codes 0x08, 0x10, ..., 0x78 (values 2^-6 .. 2^8).  Any other code
+ * (nonzero mantissa, zero, subnormal, negative, NaN) is outside the contract:
+ * its mantissa and sign bits are ignored, so C is wrong for it.  Each group
+ * runs as one-wave 128 x 128 tiles over the whole of K (no K split, no
+ * workspace).
+ * Errors: as nvfp4_gemm / nvfp4_group_gemm, plus NOT_SUPPORTED when a
+ * non-empty group has K % 128 != 0 or an SFA / SFB pointer that is not 8-byte
+ * aligned. */
+nvfp4_status nvfp4_gemm_pow2scale(const void *A, const void *SFA, const void *B, const void *SFB,
+                                  void *C, int M, int N, int K, hipStream_t stream);
+nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_groups,
+                                        hipStream_t stream);
+
 /* How a call would be carried out (host only, no HIP call).  For tests and
  * reports. */
 typedef struct {

@@ -178,3 +178,27 @@ def test_blocked_gemm_rejects_bad_arguments():
         b.NVFP4_ERROR_INVALID_VALUE
     assert lib.nvfp4_gemm_blocked(None, None, None, None, None, 0, 8, 64, None) == b.NVFP4_OK
     assert lib.nvfp4_group_gemm_blocked(None, 0, None) == b.NVFP4_OK
+
+
+# ------------------------------------------------------------ power-of-two scales
+def test_pow2scale_gemm_rejects_bad_arguments():
+    """Argument errors come back before any HIP call (no GPU needed)."""
+    lib = g.load()
+    # the FP4-MFMA path takes whole 128-K tiles and 8-byte aligned scale rows
+    assert lib.nvfp4_gemm_pow2scale(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 96, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+    assert lib.nvfp4_gemm_pow2scale(ALIGNED, ALIGNED + 4, ALIGNED, ALIGNED, ALIGNED, 8, 8, 128, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+    assert lib.nvfp4_gemm_pow2scale(ALIGNED, ALIGNED, ALIGNED, ALIGNED + 2, ALIGNED, 8, 8, 256, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+    # the general rules still apply first
+    assert lib.nvfp4_gemm_pow2scale(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 48, None) == \
+        b.NVFP4_ERROR_NOT_SUPPORTED
+    assert lib.nvfp4_gemm_pow2scale(ALIGNED, None, ALIGNED, ALIGNED, ALIGNED, 8, 8, 128, None) == \
+        b.NVFP4_ERROR_INVALID_VALUE
+    assert lib.nvfp4_gemm_pow2scale(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, -1, 8, 128, None) == \
+        b.NVFP4_ERROR_INVALID_VALUE
+    # nothing to do: no launch
+    assert lib.nvfp4_gemm_pow2scale(None, None, None, None, None, 0, 8, 128, None) == b.NVFP4_OK
+    assert lib.nvfp4_group_gemm_pow2scale(None, 0, None) == b.NVFP4_OK
+    assert lib.nvfp4_group_gemm_pow2scale(None, 1, None) == b.NVFP4_ERROR_INVALID_VALUE

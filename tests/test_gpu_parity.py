@@ -425,3 +425,72 @@ def test_group_gemm_blocked_then_plain_split(lib):
     (q,) = inputs.draw_problems(42, [(64, 64, 16384)])
     assert lib.gemm_plan(64, 64, 16384)["split_k"] > 1
     check_full(lib, q, "split after blocked")
+
+
+# ------------------------------------------------------------ power-of-two scales
+# The FP4-MFMA path for scales that are powers of two: same definition (the
+# oracle), inputs restricted to its contract (E4M3 codes with a zero mantissa).
+
+def run_pow2(lib, p):
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm_pow2scale(A, SFA, B, SFB, C, M=p.M, N=p.N, K=p.K)
+    torch.cuda.synchronize()
+    return bits(C)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (128, 128, 256), (129, 257, 384), (1, 1, 128), (64, 7168, 2048), (300, 520, 1024),
+    (256, 384, 4096), (200, 136, 0),
+])
+def test_pow2scale_matches_oracle(lib, M, N, K):
+    p = inputs.draw_problems(5600 + M + K, [(M, N, K)], inputs.POW2_SCALE_CODES)[0]
+    got = run_pow2(lib, p)
+    if K == 0:
+        assert np.all(got == 0)
+        return
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(got, c16, bound, "pow2 %dx%dx%d" % (M, N, K))
+
+
+def test_pow2scale_every_exponent(lib):
+    """All fifteen normal power-of-two codes (2^-6 .. 2^8) on each side."""
+    codes = np.arange(0x08, 0x79, 8, dtype=np.uint8)
+    for side in range(2):
+        p = inputs.draw_problems(5700 + side, [(160, 96, 512)], codes)[0]
+        # keep the other side small so no sum leaves the fp16 range
+        if side == 0:
+            p.SFB[:] = 0x08
+        else:
+            p.SFA[:] = 0x08
+        got = run_pow2(lib, p)
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "pow2 exponents side %d" % side)
+
+
+def test_pow2scale_all_ones_closed_form(lib):
+    """Codes 1.0 everywhere give C = K; SFA = 2 gives 2K; SFA = 2^8 with
+    SFB = 2^-6 gives 4K (exact in fp16 for these K)."""
+    for K, sfa, sfb, scale in [(1024, 0x38, 0x38, 1), (1024, 0x40, 0x38, 2), (512, 0x78, 0x08, 4)]:
+        M, N = 130, 70
+        A = np.full((M, K // 2), 0x22, np.uint8)
+        B = np.full((N, K // 2), 0x22, np.uint8)
+        p = inputs.Problem(M, N, K, A, np.full((M, K // 16), sfa, np.uint8), B, np.full((N, K // 16), sfb, np.uint8))
+        got = run_pow2(lib, p).view(np.float16).astype(np.float64)
+        assert np.all(got == scale * K), (K, sfa, sfb)
+
+
+def test_group_pow2scale(lib):
+    shapes = [(300, 400, 1024), (0, 64, 256), (129, 257, 2048), (200, 100, 0), (64, 640, 512)]
+    probs = inputs.draw_problems(5800, shapes, inputs.POW2_SCALE_CODES)
+    devs = [dev_problem(p) for p in probs]
+    lib.nvfp4_group_gemm_pow2scale([d + (p.M, p.N, p.K) for d, p in zip(devs, probs)])
+    torch.cuda.synchronize()
+    for i, (d, p) in enumerate(zip(devs, probs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        got = bits(d[4])
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "pow2 group %d" % i)
