@@ -70,6 +70,9 @@ def parse():
                     help="scales uniform over the 49 e4m3 codes in [0.125, 8] (default), or over their "
                          "seven powers of two, run on the FP4-MFMA path (nvfp4_gemm_pow2scale / "
                          "nvfp4_group_gemm_pow2scale)")
+    ap.add_argument("--table", choices=("host", "device"), default="host",
+                    help="grouped workloads: the problem table passed by value (default) or read on "
+                         "the device (nvfp4_group_gemm_device: plan kernel + one-wave tiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     return ap.parse_args()
@@ -208,9 +211,21 @@ def main():
         torch.cuda.synchronize()
         sets = conv
 
+    device_table = args.table == "device" and wl.grouped
+    if args.table == "device" and (not wl.grouped or blocked or pow2):
+        print("--table device applies to grouped workloads with general plain-layout scales", file=sys.stderr)
+        sys.exit(2)
     # marshal each set once; a step is then a single C call
     calls = []
     for one in sets:
+        if device_table:
+            rows = [(A, SFA, B, SFB, C, p.M, p.N, p.K) for (A, SFA, B, SFB, C), p in zip(one, probs)]
+            table = torch.frombuffer(bytearray(b.problem_table_bytes(rows)), dtype=torch.uint8).to(dev)
+            ws = torch.empty(g.nvfp4_group_gemm_device_workspace_bytes(len(one)), dtype=torch.uint8, device=dev)
+            tiles = sum(-(-p.M // 128) * -(-p.N // 128) for p in probs if p.M > 0 and p.N > 0)
+            calls.append(("device", (table.data_ptr(), len(one), tiles, ws.data_ptr(), ws.numel(), sh),
+                          (table, ws)))
+            continue
         if not wl.grouped:
             (A, SFA, B, SFB, C), p = one[0], probs[0]
             args_c = (A.data_ptr(), SFA.data_ptr(), B.data_ptr(), SFB.data_ptr(),
@@ -227,8 +242,9 @@ def main():
                 lib.nvfp4_group_gemm_pow2scale if pow2 else lib.nvfp4_group_gemm)
 
     def step(i):
-        kind, a = calls[i % len(calls)]
-        rc = gemm_fn(*a) if kind == "gemm" else group_fn(*a)
+        kind, a = calls[i % len(calls)][:2]
+        rc = (gemm_fn(*a) if kind == "gemm" else group_fn(*a) if kind == "group"
+              else lib.nvfp4_group_gemm_device(*a))
         if rc != 0:
             raise RuntimeError(g.status_string(rc))
 
@@ -293,7 +309,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS,
-                "traffic": None if blocked else measured_traffic(wl.name)}
+                "traffic": None if blocked or device_table else measured_traffic(wl.name)}
     roof["per_launch"] = {"flops": flops, "algorithmic_bytes": alg_bytes,
                           "mean_launch_us": kern_s * 1e6,
                           "event_pair_us_p10_p50_p90": [float(np.percentile(each_us, q)) for q in (10, 50, 90)],
@@ -319,7 +335,7 @@ def main():
         "config": {"workload": wl.name, "description": wl.description,
                    "shapes_MNK": shapes, "seed": 1000 + args.workload,
                    "operand_copies": copies, "scale_layout": args.scale_layout,
-                   "scales": args.scales},
+                   "scales": args.scales, "table": args.table},
         "roofline": roof,
         "cpu_baseline": cpu,
         "pct_fp4_peak": 100.0 * kern_tflops / PEAK_FP4_TFLOPS,

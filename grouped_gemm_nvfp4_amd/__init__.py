@@ -11,13 +11,17 @@ from ._binding import (  # noqa: F401
     load,
     nvfp4_blocked_scale_bytes,
     nvfp4_gemm,
+    nvfp4_gemm_batched,
     nvfp4_gemm_blocked,
     nvfp4_gemm_pow2scale,
     nvfp4_group_gemm,
     nvfp4_group_gemm_blocked,
+    nvfp4_group_gemm_device,
+    nvfp4_group_gemm_device_workspace_bytes,
     nvfp4_group_gemm_pow2scale,
     nvfp4_scales_from_blocked,
     nvfp4_scales_to_blocked,
+    problem_table_bytes,
     release_workspaces,
     status_string,
 )

@@ -24,6 +24,7 @@ EXPORTED = [
     "nvfp4_blocked_scale_bytes", "nvfp4_scales_to_blocked", "nvfp4_scales_from_blocked",
     "nvfp4_gemm_blocked", "nvfp4_group_gemm_blocked",
     "nvfp4_gemm_pow2scale", "nvfp4_group_gemm_pow2scale",
+    "nvfp4_gemm_batched", "nvfp4_group_gemm_device_workspace_bytes", "nvfp4_group_gemm_device",
 ]
 
 
@@ -90,6 +91,12 @@ def load():
     lib.nvfp4_gemm_blocked.restype = ci
     lib.nvfp4_group_gemm_blocked.argtypes = [ctypes.POINTER(Nvfp4Problem), ci, vp]
     lib.nvfp4_group_gemm_blocked.restype = ci
+    lib.nvfp4_gemm_batched.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, vp]
+    lib.nvfp4_gemm_batched.restype = ci
+    lib.nvfp4_group_gemm_device_workspace_bytes.argtypes = [ci]
+    lib.nvfp4_group_gemm_device_workspace_bytes.restype = ctypes.c_longlong
+    lib.nvfp4_group_gemm_device.argtypes = [vp, ci, ci, vp, ctypes.c_longlong, vp]
+    lib.nvfp4_group_gemm_device.restype = ci
     lib.nvfp4_gemm_pow2scale.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
     lib.nvfp4_gemm_pow2scale.restype = ci
     lib.nvfp4_group_gemm_pow2scale.argtypes = [ctypes.POINTER(Nvfp4Problem), ci, vp]
@@ -184,6 +191,37 @@ def nvfp4_group_gemm_pow2scale(problems, stream=None):
     for i, (A, SFA, B, SFB, C, M, N, K) in enumerate(problems):
         arr[i] = _problem(A, SFA, B, SFB, C, M, N, K)
     _check(load().nvfp4_group_gemm_pow2scale(arr, len(problems), _stream_handle(stream)))
+
+
+def nvfp4_gemm_batched(A, SFA, B, SFB, C, M, N, K, L, stream=None):
+    """L products of the same sizes over dense stacks of operands (batch b of A
+    at byte b*M*K/2, and so on)."""
+    _check(load().nvfp4_gemm_batched(_ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _ptr(C),
+                                     M, N, K, L, _stream_handle(stream)))
+
+
+def problem_table_bytes(problems) -> bytes:
+    """The raw bytes of an nvfp4_problem array, for a device-resident table:
+    ``problems`` is a sequence of (A, SFA, B, SFB, C, M, N, K) with tensors or
+    integer addresses."""
+    arr = (Nvfp4Problem * max(1, len(problems)))()
+    for i, (A, SFA, B, SFB, C, M, N, K) in enumerate(problems):
+        addr = [x if isinstance(x, int) or x is None else x.data_ptr() for x in (A, SFA, B, SFB, C)]
+        arr[i] = Nvfp4Problem(*addr, M, N, K)
+    return bytes(arr)[:ctypes.sizeof(Nvfp4Problem) * len(problems)]
+
+
+def nvfp4_group_gemm_device_workspace_bytes(num_groups) -> int:
+    return int(load().nvfp4_group_gemm_device_workspace_bytes(num_groups))
+
+
+def nvfp4_group_gemm_device(table, num_groups, max_tiles, workspace, stream=None):
+    """Grouped product whose problem table ``table`` (a device uint8 tensor
+    holding num_groups nvfp4_problem entries) is read on the device; the plan
+    goes into ``workspace`` (a device tensor of at least
+    nvfp4_group_gemm_device_workspace_bytes(num_groups) bytes)."""
+    _check(load().nvfp4_group_gemm_device(_ptr(table), num_groups, max_tiles, _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream_handle(stream)))
 
 
 def nvfp4_blocked_scale_bytes(rows, K) -> int:

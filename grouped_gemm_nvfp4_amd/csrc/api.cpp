@@ -6,6 +6,7 @@
 // machine without a GPU.
 #include "nvfp4.h"
 
+#include <stddef.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -550,6 +551,67 @@ nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const voi
 nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
 {
     return run(problems, num_groups, stream);
+}
+
+static_assert(sizeof(nvfp4::ProblemRecord) == sizeof(nvfp4_problem) &&
+                  offsetof(nvfp4::ProblemRecord, C) == offsetof(nvfp4_problem, C) &&
+                  offsetof(nvfp4::ProblemRecord, M) == offsetof(nvfp4_problem, M) &&
+                  offsetof(nvfp4::ProblemRecord, K) == offsetof(nvfp4_problem, K),
+              "the device reads nvfp4_problem as ProblemRecord");
+
+nvfp4_status nvfp4_gemm_batched(const void *A, const void *SFA, const void *B, const void *SFB, void *C, int M,
+                                int N, int K, int L, hipStream_t stream)
+{
+    if (L < 0 || M < 0 || N < 0 || K < 0)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (L > NVFP4_MAX_GROUPS)
+        return NVFP4_ERROR_NOT_SUPPORTED;
+    if (L == 0)
+        return NVFP4_OK;
+    // batch b of each operand starts b matrices into its dense stack
+    const uintptr_t sa = (uintptr_t)M * (uintptr_t)(K / 2), ssa = (uintptr_t)M * (uintptr_t)(K / 16);
+    const uintptr_t sb = (uintptr_t)N * (uintptr_t)(K / 2), ssb = (uintptr_t)N * (uintptr_t)(K / 16);
+    const uintptr_t sc = (uintptr_t)M * (uintptr_t)N * 2;
+    auto at = [](const void *base, uintptr_t step, int b) -> void * {
+        return base == nullptr ? nullptr : (void *)((uintptr_t)base + step * (uintptr_t)b);
+    };
+    std::vector<nvfp4_problem> probs((size_t)L);
+    for (int b = 0; b < L; ++b) {
+        nvfp4_problem &p = probs[(size_t)b];
+        p.A = at(A, sa, b);
+        p.SFA = at(SFA, ssa, b);
+        p.B = at(B, sb, b);
+        p.SFB = at(SFB, ssb, b);
+        p.C = at(C, sc, b);
+        p.M = M;
+        p.N = N;
+        p.K = K;
+    }
+    return run(probs.data(), L, stream);
+}
+
+long long nvfp4_group_gemm_device_workspace_bytes(int num_groups)
+{
+    if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS)
+        return -1;
+    return nvfp4::dev_workspace_bytes(num_groups);
+}
+
+nvfp4_status nvfp4_group_gemm_device(const nvfp4_problem *problems, int num_groups, int max_tiles, void *workspace,
+                                     long long workspace_bytes, hipStream_t stream)
+{
+    if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS || max_tiles < 0)
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (num_groups == 0 || max_tiles == 0)
+        return NVFP4_OK;
+    if (problems == nullptr || workspace == nullptr || (((uintptr_t)workspace) & 15) != 0 ||
+        workspace_bytes < nvfp4::dev_workspace_bytes(num_groups))
+        return NVFP4_ERROR_INVALID_VALUE;
+    if (max_tiles > kMaxWorkgroups)
+        return NVFP4_ERROR_NOT_SUPPORTED;
+    const hipError_t e = nvfp4::launch_device_table((const nvfp4::ProblemRecord *)problems, num_groups, max_tiles,
+                                                    workspace, stream);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
 }
 
 nvfp4_status nvfp4_gemm_pow2scale(const void *A, const void *SFA, const void *B, const void *SFB, void *C, int M,

@@ -35,6 +35,37 @@ struct GroupTable {
     GemmDesc g[kMaxGroupsPerLaunch];
 };
 
+// Device-resident grouped calls: the problem table lives in device memory
+// (written there by the caller, possibly by an earlier kernel), so the host
+// knows neither sizes nor tile counts.  A one-workgroup plan kernel turns it
+// into this table in the caller's workspace: a header, the exclusive prefix
+// over per-group tile counts (num_groups + 1 ints from byte 16), then one
+// GemmDesc per group from dev_desc_offset(num_groups).
+struct DevHeader {
+    int num_groups;
+    int total_tiles;    // tiles the table asks for (clamped to INT32_MAX)
+    int invalid_groups; // groups outside the contract, given no tiles
+    int reserved;
+};
+// Layout of nvfp4_problem as the device reads it.
+struct ProblemRecord {
+    const uint8_t *A;
+    const uint8_t *SFA;
+    const uint8_t *B;
+    const uint8_t *SFB;
+    uint16_t *C;
+    int M, N, K;
+};
+__host__ __device__ inline long long dev_desc_offset(int num_groups) { return (16 + 4LL * (num_groups + 1) + 15) / 16 * 16; }
+inline long long dev_workspace_bytes(int num_groups)
+{
+    return dev_desc_offset(num_groups) + (long long)num_groups * (long long)sizeof(GemmDesc);
+}
+// Plan kernel, then one-wave 128 x 128 tiles over a grid of max_tiles
+// workgroups (those past the table's total return at once).
+hipError_t launch_device_table(const ProblemRecord *problems, int num_groups, int max_tiles, void *workspace,
+                               hipStream_t stream);
+
 // Tile configurations the kernels are built for.
 enum TileConfig : int {
     kTile128x128 = 0,   // one wave per workgroup owning the whole 128 x 128 tile

@@ -96,6 +96,54 @@ nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const voi
 nvfp4_status nvfp4_group_gemm(const nvfp4_problem *problems, int num_groups,
                               hipStream_t stream);
 
+/* ---- Batch l > 1 (the pages' (m, n, k, l) problems: the grouped page
+ * nvfp4-group-gemm-498453, `custom_kernel` docstring and problem sizes; the
+ * single-GEMM page nvfp4-gemm-125598, `custom_kernel` and the tensor layouts
+ * (m, k, l) with strides (k, 1, m k)): L products of the same sizes whose
+ * operands are dense stacks, batch b of A at A + b M K/2 bytes, SFA + b M K/16,
+ * B + b N K/2, SFB + b N K/16, C + b M N elements.  Runs as one grouped call.
+ *   0 <= L <= NVFP4_MAX_GROUPS (more: NOT_SUPPORTED; negative: INVALID_VALUE);
+ *   L == 0 is a no-op.  Each batch obeys the single-GEMM rules above. */
+nvfp4_status nvfp4_gemm_batched(const void *A, const void *SFA, const void *B, const void *SFB,
+                                void *C, int M, int N, int K, int L, hipStream_t stream);
+
+/* ---- Device-resident problem tables (the grouped page nvfp4-group-gemm-498453
+ * keeps the per-group sizes, pointers and the CTA prefix in device tensors,
+ * `custom_kernel` host code and the group lookup in the kernel).  For callers
+ * whose group sizes are produced on the device (an MoE router's per-expert row
+ * counts) or who replay the call in a captured graph with sizes that change
+ * between replays.
+ *
+ * `problems` is a DEVICE array of num_groups nvfp4_problem entries, read by
+ * the enqueued work (not by this call), so it may be written by earlier work
+ * on the stream.  A one-workgroup plan kernel checks every entry, computes
+ * the per-group 128 x 128 tile counts and their prefix into `workspace`, then
+ * a grid of max_tiles one-wave workgroups runs the tiles (workgroups past the
+ * table's total return at once).  No allocation, no host synchronisation, no
+ * memset: the call can be captured in a HIP graph.
+ *
+ * Per-entry contract, checked on the device: M, N, K >= 0; K % 128 == 0 and
+ * K <= 2^24; when M N > 0, C present and, when K > 0, A, SFA, B, SFB present
+ * with A and B 16-byte and SFA and SFB 8-byte aligned; at most 2^24 tiles.
+ * An entry outside it gets no tiles (its C is not written) and is counted.
+ * After the work has run, the workspace starts with four int32: num_groups,
+ * the tiles the table asked for (clamped to INT32_MAX), the number of entries
+ * outside the contract, 0.  Tiles past max_tiles (total > max_tiles) are not
+ * computed: the caller bounds max_tiles from above (for an MoE layer,
+ * (tokens * top_k / 128 + num_groups) * ceil(N / 128)).
+ *
+ * workspace: device memory of at least
+ * nvfp4_group_gemm_device_workspace_bytes(num_groups) bytes, 16-byte aligned,
+ * owned by the caller; calls that overlap in time must not share it.
+ * Errors (host, before any HIP call): num_groups outside [0,
+ * NVFP4_MAX_GROUPS], max_tiles < 0, problems or workspace NULL, a misaligned
+ * or short workspace -> INVALID_VALUE; max_tiles above 2^24 - 1 ->
+ * NOT_SUPPORTED; a failed launch -> LAUNCH.  num_groups == 0 or max_tiles ==
+ * 0: nothing is enqueued (the workspace is not written). */
+long long nvfp4_group_gemm_device_workspace_bytes(int num_groups); /* -1 if num_groups is out of range */
+nvfp4_status nvfp4_group_gemm_device(const nvfp4_problem *problems, int num_groups, int max_tiles,
+                                     void *workspace, long long workspace_bytes, hipStream_t stream);
+
 /* ---- Blocked scale layout: the layout the kernelbot pages' kernels consume
  * (raw-CUDA page nvfp4-group-gemm-407526, device kernel, scale TMA issue: a
  * 128-row tile's scales start at (tile * K/64) * 512 bytes and advance 2048

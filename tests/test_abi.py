@@ -6,6 +6,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import grouped_gemm_nvfp4_amd as g
@@ -202,3 +204,54 @@ def test_pow2scale_gemm_rejects_bad_arguments():
     assert lib.nvfp4_gemm_pow2scale(None, None, None, None, None, 0, 8, 128, None) == b.NVFP4_OK
     assert lib.nvfp4_group_gemm_pow2scale(None, 0, None) == b.NVFP4_OK
     assert lib.nvfp4_group_gemm_pow2scale(None, 1, None) == b.NVFP4_ERROR_INVALID_VALUE
+
+
+# ------------------------------------------------------------ batch l and device-resident tables
+def test_batched_rejects_bad_arguments():
+    lib = g.load()
+    f = lib.nvfp4_gemm_batched
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64, -1, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, -8, 8, 64, 2, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64, 4097, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 8, 8, 48, 3, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    assert f(ALIGNED, None, ALIGNED, ALIGNED, ALIGNED, 8, 8, 64, 3, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(None, None, None, None, None, 8, 8, 64, 0, None) == b.NVFP4_OK
+    assert f(None, None, None, None, None, 0, 8, 64, 5, None) == b.NVFP4_OK
+
+
+@pytest.mark.parametrize("G", [0, 1, 2, 7, 64, 4096])
+def test_device_table_workspace_bytes(G):
+    # header (16 bytes), G + 1 prefix ints, rounded up to 16, then one
+    # 56-byte problem descriptor (5 pointers, 4 ints) per group
+    expect = (16 + 4 * (G + 1) + 15) // 16 * 16 + 56 * G
+    assert b.nvfp4_group_gemm_device_workspace_bytes(G) == expect
+
+
+def test_device_table_workspace_bytes_rejects_bad_counts():
+    assert b.nvfp4_group_gemm_device_workspace_bytes(-1) == -1
+    assert b.nvfp4_group_gemm_device_workspace_bytes(4097) == -1
+
+
+def test_device_table_call_rejects_bad_arguments():
+    lib = g.load()
+    f = lib.nvfp4_group_gemm_device
+    need = b.nvfp4_group_gemm_device_workspace_bytes(3)
+    assert f(ALIGNED, -1, 10, ALIGNED, need, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, 4097, 10, ALIGNED, 10 ** 9, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, 3, -1, ALIGNED, need, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(None, 3, 10, ALIGNED, need, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, 3, 10, None, need, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, 3, 10, ALIGNED + 8, need, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, 3, 10, ALIGNED, need - 1, None) == b.NVFP4_ERROR_INVALID_VALUE
+    assert f(ALIGNED, 3, 1 << 24, ALIGNED, need, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    # nothing to enqueue
+    assert f(None, 0, 10, None, 0, None) == b.NVFP4_OK
+    assert f(ALIGNED, 3, 0, ALIGNED, need, None) == b.NVFP4_OK
+
+
+def test_problem_table_bytes_layout():
+    raw = b.problem_table_bytes([(16, 32, 48, 64, 80, 1, 2, 128), (None, None, None, None, None, 0, 0, 0)])
+    assert len(raw) == 2 * 56
+    words = np.frombuffer(raw[:56], dtype=np.uint64)[:5]
+    assert list(words) == [16, 32, 48, 64, 80]
+    assert list(np.frombuffer(raw[40:52], dtype=np.int32)) == [1, 2, 128]

@@ -494,3 +494,101 @@ def test_group_pow2scale(lib):
             continue
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "pow2 group %d" % i)
+
+
+# ------------------------------------------------------------ batch l and device-resident tables
+
+def test_gemm_batched_matches_oracle(lib):
+    """Three batches in dense stacks (the pages' (m, k, l) layout with l
+    outermost) against the oracle batch by batch."""
+    M, N, K, L = 100, 200, 512, 3
+    probs = inputs.draw_problems(5900, [(M, N, K)] * L)
+    A = to_dev(np.stack([p.A for p in probs]))
+    SFA = to_dev(np.stack([p.SFA for p in probs]))
+    B = to_dev(np.stack([p.B for p in probs]))
+    SFB = to_dev(np.stack([p.SFB for p in probs]))
+    C = torch.full((L, M, N), -1, dtype=torch.int16, device="cuda")
+    lib.nvfp4_gemm_batched(A, SFA, B, SFB, C, M, N, K, L)
+    torch.cuda.synchronize()
+    for i, p in enumerate(probs):
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+        assert_parity(bits(C[i]), c16, bound, "batch %d" % i)
+
+
+def device_table(lib, rows):
+    raw = lib.problem_table_bytes(rows)
+    return torch.frombuffer(bytearray(raw), dtype=torch.uint8).cuda()
+
+
+def tiles_of(shapes):
+    return sum(-(-M // 128) * -(-N // 128) for (M, N, K) in shapes if M > 0 and N > 0)
+
+
+def test_group_gemm_device_table(lib):
+    shapes = [(300, 400, 1024), (0, 64, 256), (129, 257, 2048), (200, 100, 0), (64, 640, 512), (1, 1, 128)]
+    probs = inputs.draw_problems(5950, shapes)
+    devs = [dev_problem(p) for p in probs]
+    table = device_table(lib, [d + (p.M, p.N, p.K) for d, p in zip(devs, probs)])
+    G = len(shapes)
+    ws = torch.empty(lib.nvfp4_group_gemm_device_workspace_bytes(G), dtype=torch.uint8, device="cuda")
+    lib.nvfp4_group_gemm_device(table, G, tiles_of(shapes) + 7, ws)
+    torch.cuda.synchronize()
+    assert list(ws[:16].cpu().numpy().view(np.int32)) == [G, tiles_of(shapes), 0, 0]
+    for i, (d, p) in enumerate(zip(devs, probs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        got = bits(d[4])
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "device table group %d" % i)
+
+
+def test_group_gemm_device_table_skips_entries_outside_contract(lib):
+    shapes = [(128, 128, 256), (128, 128, 96), (64, 64, 256)]  # K = 96: not a multiple of 128
+    probs = inputs.draw_problems(5960, shapes)
+    devs = [dev_problem(p) for p in probs]
+    table = device_table(lib, [d + (p.M, p.N, p.K) for d, p in zip(devs, probs)])
+    ws = torch.empty(lib.nvfp4_group_gemm_device_workspace_bytes(3), dtype=torch.uint8, device="cuda")
+    lib.nvfp4_group_gemm_device(table, 3, 8, ws)
+    torch.cuda.synchronize()
+    assert list(ws[:16].cpu().numpy().view(np.int32)) == [3, 2, 1, 0]
+    assert np.all(bits(devs[1][4]) == 0xFFFF)  # not written
+    for i in (0, 2):
+        p = probs[i]
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(bits(devs[i][4]), c16, bound, "device table group %d" % i)
+
+
+def test_group_gemm_device_table_in_graph(lib):
+    """Captured once, replayed three times with the groups' M rewritten on the
+    device between replays (the table is read at run time); every replay is
+    checked against the oracle on the rows it covers."""
+    Mmax, N, K, G = 256, 384, 512, 3
+    probs = inputs.draw_problems(5970, [(Mmax, N, K)] * G)
+    devs = [dev_problem(p) for p in probs]
+    table = device_table(lib, [d + (Mmax, N, K) for d in devs])
+    words = table.view(torch.int32)  # 14 int32 per 56-byte entry, M at word 10
+    ws = torch.empty(lib.nvfp4_group_gemm_device_workspace_bytes(G), dtype=torch.uint8, device="cuda")
+    max_tiles = tiles_of([(Mmax, N, K)] * G)
+    lib.nvfp4_group_gemm_device(table, G, max_tiles, ws)  # eager run first
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.nvfp4_group_gemm_device(table, G, max_tiles, ws)
+    for ms in [(256, 64, 130), (1, 256, 0), (200, 200, 200)]:
+        for g_, m in enumerate(ms):
+            words[14 * g_ + 10] = m
+            devs[g_][4].fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert list(ws[:16].cpu().numpy().view(np.int32)) == [G, tiles_of([(m, N, K) for m in ms]), 0, 0]
+        for g_, (m, d, p) in enumerate(zip(ms, devs, probs)):
+            got = bits(d[4])
+            assert np.all(got[m:] == 0xFFFF), "rows past M written"
+            if m == 0:
+                continue
+            c16, _, bound = oracle.gemm(p.A[:m], p.SFA[:m], p.B, p.SFB, m, N, K)
+            assert_parity(got[:m], c16, bound, "graph replay M=%s group %d" % (ms, g_))
