@@ -1179,7 +1179,6 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             }
-#ifndef NVFP4_NO_SCHED_GROUPS
         __builtin_amdgcn_sched_group_barrier(0x100, 32, 0); // LDS reads
         __builtin_amdgcn_sched_group_barrier(0x002, 80, 0); // group 0 scales + step 0 decode
 #pragma unroll
@@ -1198,7 +1197,6 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-#endif
     };
 
     // power-of-two scales: step s (blocks 2 s + h of every row) of the 128-K
@@ -1545,12 +1543,10 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             void *dargs[] = {const_cast<GroupTable *>(&table)};
             return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
-#ifndef NVFP4_TILED_NO_DMA
         if (!four && vec) {
             void *dargs[] = {const_cast<GroupTable *>(&table)};
             return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
-#endif
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4, false> : (const void *)gemm_tiled_kernel<false, 4, false>)
                               : (vec ? (const void *)gemm_tiled_kernel<true, 1, false> : (const void *)gemm_tiled_kernel<false, 1, false>);
         return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
