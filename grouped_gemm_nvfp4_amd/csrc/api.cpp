@@ -62,8 +62,6 @@ struct Plan {
     std::vector<int> order;  // launch order of the groups (longest K first)
     long long total_tiles;
     long long workspace_bytes;
-    int sk_workgroups = 0;   // stream-K grid
-    long long sk_units = 0;  // stream-K (tile, K tile) units
 };
 
 // Workgroup slots of an MI355X: 256 CUs x 4 SIMDs for one-wave workgroups.
@@ -154,6 +152,14 @@ constexpr int kMaxSplitK = 16;
 // 64x2048x7168, 32x4096x4096, 64x1024x16384, 64x7168x2080; the panel kernel
 // on 64x7168x16384, 1x7168x16384, 64x16384x4096).
 constexpr int kPanelMinWorkgroups = 192;
+// Launches of M > 64 with at most this many 128 x 128 tiles also take the
+// 64-row kernels.  Measured (event means, us; 64-row route vs the one-, four-
+// wave or stream-K 128 x 128 route it replaces): 128x128x256 4.9 vs 14.2,
+// 1024x1024x4096 16.2 vs 45.2, 512x512x16384 19.5 vs 83.7, 129x257x32768 19.5
+// vs 107.7, 512x4096x7168 45.7 vs 67.1, 2048x1536x4096 (192 tiles) 46.7 vs
+// 51.6; but 1792x2048x4096 (224 tiles) 61.4 vs 52.3 and 2048x2048x4096 60.2 vs
+// 52.8.
+constexpr long long kPanelMaxTiles128 = 192;
 
 // Output tiles of every group under tile shape ts (prefix[g + 1] is the
 // running total) and the longest K in K tiles.
@@ -188,48 +194,6 @@ int small_m_split(long long total, int max_ktiles, int min_ktiles)
         return 1;
     return (int)std::min<long long>(
         {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles / min_ktiles), (long long)kMaxSplitK});
-}
-
-// Stream-K for one-wave 128 x 128 tiles: P workgroups (one per SIMD at most,
-// at least kMinUnitsPerWorkgroup K tiles each) take equal shares of the
-// launch's (tile, K tile) units.  Each shared tile costs its contributors a
-// write-through store of a 64 KiB partial tile and its last contributor the
-// serial read of all of them: measured, about kFixupUnits K tiles of time plus
-// half a K tile per contributor, and more when a thousand workgroups do it at
-// once (the 8-group MoE and 2-group workloads ran 1.2x and 1.7x slower with
-// it).  So it is taken only for at most kMaxStreamKTiles tiles and when the
-// model -- U / P units plus that cost -- beats the four-wave form and is at
-// most 2/3 of the dispatcher's list schedule of whole one-wave tiles
-// (512x512x16384: 113 us four-wave, 86 us stream-K; 256x1024x8192: 67 us
-// four-wave, 73 us stream-K).
-constexpr int kMinUnitsPerWorkgroup = 16;
-constexpr int kFixupUnits = 8;
-constexpr long long kMaxStreamKTiles = 256;
-
-// Stream-K estimate in quarter K tiles (the unit of the makespans below), or
-// -1 where stream-K does not apply; sets *P to its grid.
-long long stream_k_makespan(const nvfp4_problem *problems, const Plan &plan, const nvfp4::TileShape &ts, int *P_out)
-{
-    const int num_groups = (int)plan.prefix.size() - 1;
-    int launched = 0;
-    for (int g = 0; g < num_groups; ++g)
-        launched += plan.prefix[g + 1] > plan.prefix[g];
-    if (plan.total_tiles > kMaxStreamKTiles || launched > nvfp4::kMaxGroupsPerLaunch)
-        return -1;
-    long long units = 0, max_kt = 1;
-    for (int gi : plan.order) {
-        const long long t = plan.prefix[gi + 1] - plan.prefix[gi];
-        if (t == 0)
-            continue;
-        const long long kt = std::max(1, (problems[gi].K + ts.tile_k - 1) / ts.tile_k);
-        units += t * kt;
-        max_kt = std::max(max_kt, kt);
-    }
-    const long long P = std::max(1LL, std::min<long long>(kWaveSlots, units / kMinUnitsPerWorkgroup));
-    const long long per_wg = (units + P - 1) / P;
-    const long long contributors = (max_kt + per_wg - 1) / per_wg + 1;
-    *P_out = (int)P;
-    return 4 * (per_wg + kFixupUnits + (contributors + 1) / 2);
 }
 
 // pow2: the power-of-two-scale path (one-wave 128 x 128 tiles on the scaled
@@ -276,7 +240,21 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         plan->workspace_bytes = 0;
         return NVFP4_OK;
     }
-    if (max_m > 0 && max_m <= 64) {
+    // Few 128 x 128 tiles: the 64-row kernels (eight waves per workgroup, two
+    // per SIMD, K split within and across workgroups) fill the chip where one
+    // wave per 128 x 128 tile would leave most SIMDs idle and run each tile's
+    // K serially at the one-wave issue rate.
+    bool few_tiles = false;
+    if (max_m > 64) {
+        std::vector<int> prefix128;
+        long long total128 = 0;
+        int kt128 = 0;
+        s = count_tiles(problems, num_groups, nvfp4::tile_shape(nvfp4::kTile128x128), &prefix128, &total128, &kt128);
+        if (s != NVFP4_OK)
+            return s;
+        few_tiles = total128 <= kPanelMaxTiles128;
+    }
+    if (max_m > 0 && (max_m <= 64 || few_tiles)) {
         // panel: each wave takes at least one 256-K tile of a slice (8 waves)
         plan->cfg = nvfp4::kPanel64x64;
         s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
@@ -314,10 +292,10 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         if (!empty_output(problems[g]) && problems[g].K < 4 * ts.tile_k)
             four_ok = false;
     if (plan->cfg == nvfp4::kTile128x128 && total > 0 && total < 4 * kWaveSlots) {
-        // Few tiles: compare one wave per tile (kWaveSlots slots), four waves
-        // splitting each tile's K (kWaveSlots / 4 slots, a quarter of the K
-        // tiles each, plus about 3% for adding the sums) and stream-K, all in
-        // quarter K tiles.
+        // Fewer tiles than one-wave slots times four: compare one wave per tile
+        // (kWaveSlots slots) with four waves splitting each tile's K
+        // (kWaveSlots / 4 slots, a quarter of the K tiles each, plus about 3%
+        // for adding the sums), both in quarter K tiles.
         std::vector<std::pair<long long, long long>> g1, g4;
         for (int gi : plan->order) {
             const nvfp4_problem &p = problems[gi];
@@ -330,26 +308,14 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         }
         const long long m1 = list_makespan(g1, kWaveSlots);
         const long long m4 = four_ok ? list_makespan(g4, kWaveSlots / 4) * 103 / 100 : -1;
-        int P = 0;
-        const long long msk = stream_k_makespan(problems, *plan, ts, &P);
         // Measured: per K tile the four-wave form is slower than four
         // independent one-wave workgroups (the 8-group and 2-group workloads
         // ran 10-17% slower with it), so it is taken only where the model
-        // promises at least a factor of two: few, long tiles (there it wins
-        // 1.4-3.4x: 256x384x1024, 1000x520x1184, 512x512x16384).
-        if (msk >= 0 && 3 * msk <= 2 * m1 && (m4 < 0 || msk < m4)) {
-            plan->cfg = nvfp4::kTile128x128SK;
-            plan->sk_workgroups = P;
-            long long units = 0;
-            for (int gi : plan->order)
-                units += (long long)(plan->prefix[gi + 1] - plan->prefix[gi]) *
-                         std::max(1, (problems[gi].K + ts.tile_k - 1) / ts.tile_k);
-            plan->sk_units = units;
-        } else if (m4 >= 0 && 2 * m4 < m1) {
+        // promises at least a factor of two.
+        if (m4 >= 0 && 2 * m4 < m1)
             plan->cfg = nvfp4::kTile128x128K4;
-        }
     }
-    plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k, plan->sk_workgroups);
+    plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
     return NVFP4_OK;
 }
 
@@ -357,13 +323,12 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
 {
     info->kernel = plan.total_tiles == 0 ? 0
                    : plan.split_k > 1 ? 2
-                   : plan.cfg == nvfp4::kTile128x128K4 ? 3
-                   : plan.cfg == nvfp4::kTile128x128SK ? 4 : 1;
+                   : plan.cfg == nvfp4::kTile128x128K4 ? 3 : 1;
     info->tile_m = plan.tile_m;
     info->tile_n = plan.tile_n;
     info->split_k = plan.split_k;
     info->total_tiles = (int)plan.total_tiles;
-    info->workgroups = plan.cfg == nvfp4::kTile128x128SK ? plan.sk_workgroups : (int)(plan.total_tiles * plan.split_k);
+    info->workgroups = (int)(plan.total_tiles * plan.split_k);
     info->workspace_bytes = plan.workspace_bytes;
 }
 
@@ -388,8 +353,7 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
             return NVFP4_OK;
         table.num_groups = n;
         // launches of one call share the workspace: stream order keeps them apart
-        table.units = (int)plan.sk_units;
-        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, workspace, plan.sk_workgroups, stream);
+        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, workspace, stream);
         n = 0;
         table.prefix[0] = 0;
         return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;

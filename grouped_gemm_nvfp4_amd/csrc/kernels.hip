@@ -144,338 +144,215 @@ constexpr int kCoherent = 16;
 
 // kWaves = 1: one wave owns a 128 x 128 tile.  kWaves = 4: four waves split
 // each tile's K and add their sums through LDS.
-//
-// kStreamK (one-wave workgroups): the launch's work is the list of (tile,
-// 128-K tile) units, tiles in launch order; workgroup p of P takes units
-// [p U / P, (p+1) U / P), i.e. pieces of consecutive tiles, so every SIMD gets
-// the same number of K tiles whatever the tile count.  A tile whose units all
-// fall to one workgroup is written directly.  A tile shared by several
-// workgroups: each stores its fp32 partial tile in one of its two slots (slot
-// 0 for its first piece, 1 for its last), then takes a ticket from the tile's
-// counter; the one that draws the last ticket adds the contributors' partial
-// tiles in workgroup order (the result does not depend on arrival order),
-// writes C and resets the counter to zero.
-template <bool kVec, int kWaves, bool kStreamK>
+template <bool kVec, int kWaves>
 __global__ __launch_bounds__(64 * kWaves) void gemm_tiled_kernel(GroupTable tab, float *partials, int *counters)
 {
-    static_assert(!kStreamK || kWaves == 1, "stream-K runs one-wave workgroups");
     using namespace tiled;
     __shared__ __attribute__((aligned(16))) uint8_t lds_all[kWaves * 2 * kStageBytes];
 
     const int wave = kWaves == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     uint8_t *lds = lds_all + wave * 2 * kStageBytes; // this wave's stages
 
-    // stream-K: this workgroup's units [u_lo, u_hi)
-    const long P = gridDim.x;
-    const long U = tab.units;
-    const long u_lo = kStreamK ? (long)blockIdx.x * U / P : 0;
-    const long u_hi = kStreamK ? (long)(blockIdx.x + 1) * U / P : 0;
-    long u = u_lo;
-
     f32x16 acc[4][4];
 
-    for (;;) {
-        // The lane index passes through an empty asm statement each trip, so
-        // the lane-dependent addresses below are recomputed per piece instead
-        // of being hoisted out of this loop and kept live (they would spill).
-        int lane = (int)threadIdx.x & 63;
-        if (kStreamK)
-            __asm__ volatile("" : "+v"(lane));
-        const int h = lane >> 5;
-        const int l32 = lane & 31;
-        const int crow = lane >> 2, c16 = lane & 3;
-        const uint32_t sh = h * 16;
+    const int lane = (int)threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int crow = lane >> 2, c16 = lane & 3;
+    const uint32_t sh = h * 16;
 
-        // the piece: launch-wide tile w, its K tiles [kb0, kb1) of kt_tile
-        int w, gi, kb0, kb1, kt_tile;
-        long tile_u0 = 0;
-        if (kStreamK) {
-            if (u >= u_hi)
-                break;
-            // the group of unit u (a tile has max(1, ceil(K / BK)) units, so
-            // a K = 0 tile still gets its zero C)
-            long base = 0;
-            gi = 0;
-            for (;;) {
-                const int kt_g = max(1, (tab.g[gi].K + BK - 1) / BK);
-                const long units_g = (long)(tab.prefix[gi + 1] - tab.prefix[gi]) * kt_g;
-                if (u < base + units_g || gi == tab.num_groups - 1) {
-                    kt_tile = kt_g;
-                    break;
-                }
-                base += units_g;
-                ++gi;
-            }
-            const int tile_in_g = (int)((u - base) / kt_tile);
-            w = tab.prefix[gi] + tile_in_g;
-            tile_u0 = base + (long)tile_in_g * kt_tile;
-            kb0 = (int)(u - tile_u0);
-            kb1 = (int)min((long)kt_tile, kb0 + (u_hi - u));
-            u = tile_u0 + kb1;
-        } else {
-            w = blockIdx.x;
-            gi = find_group(tab, w);
-            kt_tile = (tab.g[gi].K + BK - 1) / BK;
-            // this wave's share of the tile's K tiles
-            kb0 = (int)((long)kt_tile * wave / kWaves);
-            kb1 = (int)((long)kt_tile * (wave + 1) / kWaves);
+    // the tile and this wave's share [kb0, kb1) of its kt_tile K tiles
+    const int w = blockIdx.x;
+    const int gi = find_group(tab, w);
+    const int kt_tile = (tab.g[gi].K + BK - 1) / BK;
+    const int kb0 = (int)((long)kt_tile * wave / kWaves);
+    const int kb1 = (int)((long)kt_tile * (wave + 1) / kWaves);
+    const GemmDesc &d = tab.g[gi];
+    const int r = w - tab.prefix[gi];
+    const int tm = r % d.tiles_m;
+    const int tn = r / d.tiles_m;
+    const int M = d.M, N = d.N, K = d.K;
+    const int row0 = tm * BM, col0 = tn * BN;
+
+    const int kb_row = K / 2;
+    const int ks_row = K / 16;
+    const int kt_base = kb0;
+    const int nkt = kb1 - kb0;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
+    const uint32_t line_off = (uint32_t)(crow * kb_row + c16 * 16);
+
+    auto load = [&](TiledSlot &s, int kt) {
+        const bool live = kt < nkt;
+        const int kb = (kt_base + kt) * kRowBytes, ks = (kt_base + kt) * kSfBytes;
+        const bool cin = live && (kb + c16 * 16) < kb_row; // chunk inside K
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = cin ? line_off + (uint32_t)(16 * j * kb_row + kb) : kOutOfRange;
+            s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+            s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
         }
-        const GemmDesc &d = tab.g[gi];
-        const int r = w - tab.prefix[gi];
-        const int tm = r % d.tiles_m;
-        const int tn = r / d.tiles_m;
-        const int M = d.M, N = d.N, K = d.K;
-        const int row0 = tm * BM, col0 = tn * BN;
-
-        const int kb_row = K / 2;
-        const int ks_row = K / 16;
-        const int kt_base = kb0;
-        const int nkt = kb1 - kb0;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
-        const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
-        const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
-        const uint32_t line_off = (uint32_t)(crow * kb_row + c16 * 16);
-
-        auto load = [&](TiledSlot &s, int kt) {
-            const bool live = kt < nkt;
-            const int kb = (kt_base + kt) * kRowBytes, ks = (kt_base + kt) * kSfBytes;
-            const bool cin = live && (kb + c16 * 16) < kb_row; // chunk inside K
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t off = cin ? line_off + (uint32_t)(16 * j * kb_row + kb) : kOutOfRange;
-                s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
-                s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
-            }
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t row = (uint32_t)(64 * j + lane);
+            if (kVec) {
+                const uint32_t off = live ? row * ks_row + ks : kOutOfRange;
+                s.sa[j] = __builtin_amdgcn_raw_buffer_load_b64(rSA, off, 0, 0);
+                s.sb[j] = __builtin_amdgcn_raw_buffer_load_b64(rSB, off, 0, 0);
+            } else {
+                uint32_t va[4], vb[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t row = (uint32_t)(64 * j + lane);
-                if (kVec) {
-                    const uint32_t off = live ? row * ks_row + ks : kOutOfRange;
-                    s.sa[j] = __builtin_amdgcn_raw_buffer_load_b64(rSA, off, 0, 0);
-                    s.sb[j] = __builtin_amdgcn_raw_buffer_load_b64(rSB, off, 0, 0);
-                } else {
-                    uint32_t va[4], vb[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const bool ok = live && (ks + 2 * p) < ks_row;
-                        const uint32_t off = ok ? row * ks_row + ks + 2 * p : kOutOfRange;
-                        va[p] = __builtin_amdgcn_raw_buffer_load_b16(rSA, off, 0, 0);
-                        vb[p] = __builtin_amdgcn_raw_buffer_load_b16(rSB, off, 0, 0);
-                    }
-                    s.sa[j] = (u32x2){va[0] | (va[1] << 16), va[2] | (va[3] << 16)};
-                    s.sb[j] = (u32x2){vb[0] | (vb[1] << 16), vb[2] | (vb[3] << 16)};
+                for (int p = 0; p < 4; ++p) {
+                    const bool ok = live && (ks + 2 * p) < ks_row;
+                    const uint32_t off = ok ? row * ks_row + ks + 2 * p : kOutOfRange;
+                    va[p] = __builtin_amdgcn_raw_buffer_load_b16(rSA, off, 0, 0);
+                    vb[p] = __builtin_amdgcn_raw_buffer_load_b16(rSB, off, 0, 0);
                 }
+                s.sa[j] = (u32x2){va[0] | (va[1] << 16), va[2] | (va[3] << 16)};
+                s.sb[j] = (u32x2){vb[0] | (vb[1] << 16), vb[2] | (vb[3] << 16)};
             }
-        };
+        }
+    };
 
-        auto put = [&](const TiledSlot &s, int buf) {
-            uint8_t *st = lds + buf * kStageBytes;
+    auto put = [&](const TiledSlot &s, int buf) {
+        uint8_t *st = lds + buf * kStageBytes;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                *(u32x4 *)(st + kAOff + swz(16 * j + crow, c16)) = s.a[j];
-                *(u32x4 *)(st + kBOff + swz(16 * j + crow, c16)) = s.b[j];
-            }
+        for (int j = 0; j < 8; ++j) {
+            *(u32x4 *)(st + kAOff + swz(16 * j + crow, c16)) = s.a[j];
+            *(u32x4 *)(st + kBOff + swz(16 * j + crow, c16)) = s.b[j];
+        }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                *(u32x2 *)(st + kSaOff + (64 * j + lane) * kSfBytes) = s.sa[j];
-                *(u32x2 *)(st + kSbOff + (64 * j + lane) * kSfBytes) = s.sb[j];
-            }
-        };
+        for (int j = 0; j < 2; ++j) {
+            *(u32x2 *)(st + kSaOff + (64 * j + lane) * kSfBytes) = s.sa[j];
+            *(u32x2 *)(st + kSbOff + (64 * j + lane) * kSfBytes) = s.sb[j];
+        }
+    };
 
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = (f32x16){};
+
+    // MFMA work of one 64-K group g of the tile in stage buf
+    auto compute = [&](int buf, int g) {
+        const uint8_t *st = lds + buf * kStageBytes;
+        // scale pairs of this lane's half of group g: blocks 4g+2h, 4g+2h+1
+        half2_t ca[4], cb[4];
+        u32x4 pa[4], pb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
+            const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
+            ca[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
+            cb[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
+            pa[i] = *(const u32x4 *)(st + kAOff + swz(32 * i + l32, 2 * g + h));
+            pb[i] = *(const u32x4 *)(st + kBOff + swz(32 * i + l32, 2 * g + h));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            half8_t fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa[i] = decode8(pa[i][q], q < 2 ? bcast_lo(ca[i]) : bcast_hi(ca[i]));
+                fb[i] = decode8(pb[i][q], q < 2 ? bcast_lo(cb[i]) : bcast_hi(cb[i]));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    if (nkt > 0) {
+        TiledSlot x;
+        load(x, 0);
+        put(x, 0);
+        load(x, 1);
+        for (int kt = 0; kt < nkt; ++kt) {
+            // stage kt&1 holds tile kt; x holds tile kt + 1 (in flight).  The
+            // refill sits between the two halves so that it issues while the
+            // first half's MFMAs run.
+            compute(kt & 1, 0);
+            put(x, (kt + 1) & 1);
+            load(x, kt + 2);
+            compute(kt & 1, 1);
+        }
+    }
+
+    if (kWaves > 1) {
+        // add the waves' sums: 3 -> 1 and 2 -> 0, then 1 -> 0, through LDS in
+        // register order ([reg][lane]: full 256-byte rows, conflict free)
+        float *red = (float *)lds_all;
+        constexpr int kAccFloats = 4 * 4 * 16 * 64;
+        __syncthreads();
+#pragma unroll
+        for (int round = 0; round < 2; ++round) {
+            const int give_lo = round == 0 ? 2 : 1; // waves [give_lo, 2 give_lo) hand over
+            if (wave >= give_lo && wave < 2 * give_lo) {
+                float *dst = red + (wave - give_lo) * kAccFloats + lane;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            dst[((i * 4 + j) * 16 + e) * 64] = acc[i][j][e];
+            }
+            __syncthreads();
+            if (wave < give_lo) {
+                const float *src = red + wave * kAccFloats + lane;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[i][j][e] += src[((i * 4 + j) * 16 + e) * 64];
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue: fp32 -> fp16 (round to nearest even) into LDS by wave 0, then
+    // 16-byte row-contiguous stores masked to M x N by all waves.
+    uint8_t *sC = lds_all;
+    if (wave == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = (f32x16){};
-
-        // MFMA work of one 64-K group g of the tile in stage buf
-        auto compute = [&](int buf, int g) {
-            const uint8_t *st = lds + buf * kStageBytes;
-            // scale pairs of this lane's half of group g: blocks 4g+2h, 4g+2h+1
-            half2_t ca[4], cb[4];
-            u32x4 pa[4], pb[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
-                const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
-                ca[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
-                cb[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
-                pa[i] = *(const u32x4 *)(st + kAOff + swz(32 * i + l32, 2 * g + h));
-                pb[i] = *(const u32x4 *)(st + kBOff + swz(32 * i + l32, 2 * g + h));
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                half8_t fa[4], fb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fa[i] = decode8(pa[i][q], q < 2 ? bcast_lo(ca[i]) : bcast_hi(ca[i]));
-                    fb[i] = decode8(pb[i][q], q < 2 ? bcast_lo(cb[i]) : bcast_hi(cb[i]));
+                for (int e = 0; e < 16; ++e) {
+                    const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
+                    const int col = 32 * j + l32;
+                    *(uint16_t *)(sC + row * kCStride + col * 2) =
+                        __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            }
-        };
-
-        if (nkt > 0) {
-            TiledSlot x;
-            load(x, 0);
-            put(x, 0);
-            load(x, 1);
-            for (int kt = 0; kt < nkt; ++kt) {
-                // stage kt&1 holds tile kt; x holds tile kt + 1 (in flight).  The
-                // refill sits between the two halves so that it issues while the
-                // first half's MFMAs run.
-                compute(kt & 1, 0);
-                put(x, (kt + 1) & 1);
-                load(x, kt + 2);
-                compute(kt & 1, 1);
-            }
-        }
-
-        if (kWaves > 1) {
-            // add the waves' sums: 3 -> 1 and 2 -> 0, then 1 -> 0, through LDS in
-            // register order ([reg][lane]: full 256-byte rows, conflict free)
-            float *red = (float *)lds_all;
-            constexpr int kAccFloats = 4 * 4 * 16 * 64;
-            __syncthreads();
-#pragma unroll
-            for (int round = 0; round < 2; ++round) {
-                const int give_lo = round == 0 ? 2 : 1; // waves [give_lo, 2 give_lo) hand over
-                if (wave >= give_lo && wave < 2 * give_lo) {
-                    float *dst = red + (wave - give_lo) * kAccFloats + lane;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-#pragma unroll
-                            for (int e = 0; e < 16; ++e)
-                                dst[((i * 4 + j) * 16 + e) * 64] = acc[i][j][e];
-                }
-                __syncthreads();
-                if (wave < give_lo) {
-                    const float *src = red + wave * kAccFloats + lane;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-#pragma unroll
-                            for (int e = 0; e < 16; ++e)
-                                acc[i][j][e] += src[((i * 4 + j) * 16 + e) * 64];
-                }
-                __syncthreads();
-            }
-        }
-
-        if (kStreamK && !(kb0 == 0 && kb1 == kt_tile)) {
-            // a shared tile: partial tiles are [16-byte lane piece (i, j, e/4)][lane]
-            const long p_self = blockIdx.x;
-            const long p_first = ((tile_u0 + 1) * P - 1) / U;
-            const long p_last = ((tile_u0 + kt_tile) * P - 1) / U;
-            auto slot_of = [&](long q) { return (q * U / P >= tile_u0) ? 0 : 1; };
-            constexpr int kTileBytes = BM * BN * 4;
-            {
-                const __amdgpu_buffer_rsrc_t rP =
-                    make_rsrc((uint8_t *)partials + (p_self * 2 + slot_of(p_self)) * (long)kTileBytes, kTileBytes);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const u32x4 v = __builtin_bit_cast(
-                                u32x4, (float4){acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]});
-                            // constant part in the scalar offset, lane part in the vector one
-                            __builtin_amdgcn_raw_buffer_store_b128(v, rP, (uint32_t)(lane * 16),
-                                                                   ((i * 4 + j) * 4 + e) * 1024, kCoherent);
-                        }
-            }
-            __builtin_amdgcn_s_waitcnt(0); // the stores have completed
-            int ticket = 0;
-            if (lane == 0)
-                ticket = __hip_atomic_fetch_add(counters + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ticket = __builtin_amdgcn_readfirstlane(ticket);
-            if (ticket != (int)(p_last - p_first))
-                continue; // another workgroup finishes this tile
-            // the last contributor: sum the partial tiles in workgroup order
-            // (from zero), a quarter tile (64 values per lane) of loads in
-            // flight at a time
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = (f32x16){};
-            for (long q = p_first; q <= p_last; ++q) {
-                const __amdgpu_buffer_rsrc_t rQ =
-                    make_rsrc((uint8_t *)partials + (q * 2 + slot_of(q)) * (long)kTileBytes, kTileBytes);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    u32x4 t[4][4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            t[j][e] = __builtin_amdgcn_raw_buffer_load_b128(rQ, (uint32_t)(lane * 16),
-                                                                            ((i * 4 + j) * 4 + e) * 1024, kCoherent);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float4 f = __builtin_bit_cast(float4, t[j][e]);
-                            acc[i][j][4 * e] += f.x;
-                            acc[i][j][4 * e + 1] += f.y;
-                            acc[i][j][4 * e + 2] += f.z;
-                            acc[i][j][4 * e + 3] += f.w;
-                        }
-                    SCHED_FENCE();
-                }
-            }
-            if (lane == 0)
-                __hip_atomic_store(counters + w, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-
-        // epilogue: fp32 -> fp16 (round to nearest even) into LDS by wave 0, then
-        // 16-byte row-contiguous stores masked to M x N by all waves.
-        uint8_t *sC = lds_all;
-        if (wave == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
-                        const int col = 32 * j + l32;
-                        *(uint16_t *)(sC + row * kCStride + col * 2) =
-                            __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
-                    }
-        }
-        if (kWaves > 1)
-            __syncthreads();
-        const bool vec_ok = (N % 8 == 0) && ((((uintptr_t)d.C) & 15) == 0);
+    }
+    if (kWaves > 1)
+        __syncthreads();
+    const bool vec_ok = (N % 8 == 0) && ((((uintptr_t)d.C) & 15) == 0);
 #pragma unroll 4
-        for (int s = 0; s < BM * BN / 8 / (64 * kWaves); ++s) {
-            const int seg = s * 64 * kWaves + (int)threadIdx.x;
-            const int row = seg >> 4, c8 = (seg & 15) * 8;
-            const int grow = row0 + row, gcol = col0 + c8;
-            if (grow >= M)
-                continue;
-            uint16_t *dst = d.C + (long)grow * N + gcol;
-            const uint16_t *src = (const uint16_t *)(sC + row * kCStride + c8 * 2);
-            if (vec_ok && gcol + 8 <= N) {
-                *(u32x4 *)dst = *(const u32x4 *)src;
-            } else {
+    for (int s = 0; s < BM * BN / 8 / (64 * kWaves); ++s) {
+        const int seg = s * 64 * kWaves + (int)threadIdx.x;
+        const int row = seg >> 4, c8 = (seg & 15) * 8;
+        const int grow = row0 + row, gcol = col0 + c8;
+        if (grow >= M)
+            continue;
+        uint16_t *dst = d.C + (long)grow * N + gcol;
+        const uint16_t *src = (const uint16_t *)(sC + row * kCStride + c8 * 2);
+        if (vec_ok && gcol + 8 <= N) {
+            *(u32x4 *)dst = *(const u32x4 *)src;
+        } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (gcol + e < N)
-                        dst[e] = src[e];
-            }
+            for (int e = 0; e < 8; ++e)
+                if (gcol + e < N)
+                    dst[e] = src[e];
         }
-        if (!kStreamK)
-            break;
     }
 }
 
@@ -1491,8 +1368,7 @@ __global__ __launch_bounds__(256) void scale_conversion_kernel(ScaleConvTable ta
 
 } // namespace
 
-hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, int sk_workgroups,
-                          hipStream_t stream)
+hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, hipStream_t stream)
 {
     const int tiles = table.prefix[table.num_groups];
     const int total = tiles * table.split_k;
@@ -1522,7 +1398,6 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         return hipLaunchKernel(fn, dim3(total), dim3(panel::kThreads), args, 0, stream);
     }
     case kTile128x128K4:
-    case kTile128x128SK:
     case kTile128x128Pow2:
     case kTile128x128:
     default: {
@@ -1530,12 +1405,6 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % tiled::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 7) == 0;
-        if (cfg == kTile128x128SK) {
-            if (workspace == nullptr || tiles > kMaxSplitTiles || sk_workgroups <= 0)
-                return hipErrorInvalidValue;
-            const void *fn = vec ? (const void *)gemm_tiled_kernel<true, 1, true> : (const void *)gemm_tiled_kernel<false, 1, true>;
-            return hipLaunchKernel(fn, dim3(sk_workgroups), dim3(64), args, 0, stream);
-        }
         const bool four = cfg == kTile128x128K4;
         if (cfg == kTile128x128Pow2) {
             if (!vec)
@@ -1547,8 +1416,8 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             void *dargs[] = {const_cast<GroupTable *>(&table)};
             return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
-        const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4, false> : (const void *)gemm_tiled_kernel<false, 4, false>)
-                              : (vec ? (const void *)gemm_tiled_kernel<true, 1, false> : (const void *)gemm_tiled_kernel<false, 1, false>);
+        const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
+                              : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);
         return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
     }
     }

@@ -30,7 +30,6 @@ constexpr int kMaxGroupsPerLaunch = 64;
 struct GroupTable {
     int num_groups;
     int split_k;                         // K slices per tile (1: no split)
-    int units;                           // stream-K: (tile, K tile) units of the launch
     int prefix[kMaxGroupsPerLaunch + 1]; // in output tiles
     GemmDesc g[kMaxGroupsPerLaunch];
 };
@@ -72,7 +71,6 @@ enum TileConfig : int {
     kStream64x32 = 1,   // 8 waves split K; each streams its own share; K may be split
     kTile128x128K4 = 2, // 128 x 128 tile, four waves splitting its K, sums added in LDS
     kPanel64x64 = 3,    // 8 waves split K, each owning the 64 x 64 tile; K may be split
-    kTile128x128SK = 4, // one-wave 128 x 128 tiles, stream-K: equal (tile, K tile) shares
     kTile128x128Pow2 = 5, // one-wave 128 x 128 tiles on the scaled FP4 MFMA (power-of-two scales)
 };
 
@@ -88,7 +86,6 @@ inline TileShape tile_shape(TileConfig c)
     case kPanel64x64:
         return {64, 64, 256};
     case kTile128x128K4:
-    case kTile128x128SK:
     case kTile128x128Pow2:
     case kTile128x128:
     default:
@@ -103,24 +100,19 @@ inline long long partial_elems(TileConfig c)
     return (long long)t.tile_m * t.tile_n;
 }
 
-// Device workspace of a K-split or stream-K launch (bytes): kMaxSplitTiles
-// tile counters (zero when the workspace is allocated; a kernel that uses
-// them leaves them zero), then the fp32 partial tiles: of every (tile, K
-// slice) for a K split, two per workgroup for stream-K.  Such launches have at
-// most kMaxSplitTiles tiles.
+// Device workspace of a K-split launch (bytes): kMaxSplitTiles tile counters
+// (zero when the workspace is allocated; a kernel that uses them leaves them
+// zero), then the fp32 partial tiles of every (tile, K slice).  Such launches
+// have at most kMaxSplitTiles tiles.
 constexpr int kMaxSplitTiles = 4096;
 constexpr long long kCounterBytes = kMaxSplitTiles * 4;
-inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k, int sk_workgroups)
+inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k)
 {
-    if (c == kTile128x128SK)
-        return kCounterBytes + 2LL * sk_workgroups * partial_elems(c) * 4;
     return split_k > 1 ? kCounterBytes + total_tiles * split_k * partial_elems(c) * 4 : 0;
 }
 
-// Launches one grouped pass (table already filled, prefix included, units
-// set for stream-K).  sk_workgroups: the stream-K grid (kTile128x128SK only).
-hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, int sk_workgroups,
-                          hipStream_t stream);
+// Launches one grouped pass (table already filled, prefix included).
+hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, hipStream_t stream);
 
 // Scale-layout conversion, batched: entry e moves the scales of a
 // rows[e] x (kb[e] = K/16) matrix between the plain [rows][K/16] layout and

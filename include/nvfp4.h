@@ -211,14 +211,13 @@ nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_g
  * reports. */
 typedef struct {
     int kernel;      /* 0: nothing to launch, 1: one tile per workgroup, 2: K split
-                        across workgroups, 3: K split across a workgroup's waves,
-                        4: stream-K (equal shares of all (tile, K tile) units) */
+                        across workgroups, 3: a 128 x 128 tile's K split across
+                        the workgroup's four waves */
     int tile_m;      /* output rows per workgroup */
     int tile_n;      /* output columns per workgroup */
     int split_k;     /* K slices per output tile (1 = none) */
     int total_tiles; /* output tiles over all groups */
-    int workgroups;  /* workgroups launched (total_tiles * split_k; for
-                        stream-K the grid of workgroups sharing the units) */
+    int workgroups;  /* workgroups launched (total_tiles * split_k) */
     long long workspace_bytes; /* device workspace the call needs */
 } nvfp4_plan_info;
 

@@ -113,7 +113,7 @@ def test_small_m_split_k_shapes(lib, M, N, K):
 
 @pytest.mark.parametrize("M,N,K,kernel", [
     (1024, 65536, 128, 1),   # >= 4096 tiles: one wave per 128x128 tile
-    (1000, 520, 1184, 3),    # few tiles: four waves split each tile's K
+    (1800, 2000, 1184, 3),   # 240 tiles: four waves split each tile's K (ragged M, N and K)
 ])
 def test_tiled_variants(lib, M, N, K, kernel):
     info = lib.gemm_plan(M, N, K)
@@ -160,22 +160,23 @@ def test_scale_pointers_at_odd_offsets(lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (512, 512, 16384),   # 16 tiles, 2048 units over 128 workgroups
-    (300, 520, 16384),   # 15 ragged tiles
-    (129, 257, 32768),   # 6 tiles, mostly padding rows and columns
+    (128, 128, 256),     # one 128 x 128 tile: eight 64 x 32 tiles
+    (512, 512, 16384),   # 16 tiles of 128 x 128: 64 x 64 tiles, K split in four
+    (300, 520, 16384),   # ragged M and N, K split in five
+    (129, 257, 32768),   # mostly padding rows and columns, K split in sixteen
 ])
-def test_stream_k_shapes(lib, M, N, K):
-    """Few 128 x 128 tiles with long K: workgroups take equal shares of the
-    (tile, K tile) units and shared tiles are summed by the last arriver."""
+def test_few_tiles_take_64_row_kernels(lib, M, N, K):
+    """M > 64 with at most 192 tiles of 128 x 128 runs on the 64-row kernels
+    (eight waves per workgroup, K split within and across workgroups)."""
     info = lib.gemm_plan(M, N, K)
-    assert info["kernel"] == 4 and info["workgroups"] > info["total_tiles"]
+    assert info["tile_m"] == 64
     p = inputs.draw_problems(5200 + M + K, [(M, N, K)])[0]
-    check_full(lib, p, "stream-K %dx%dx%d" % (M, N, K))
+    check_full(lib, p, "few tiles %dx%dx%d split %d" % (M, N, K, info["split_k"]))
 
 
-def test_stream_k_deterministic(lib):
-    """The last arriver adds the partial tiles in workgroup order, so repeated
-    calls agree bit for bit whatever order the workgroups finish in."""
+def test_few_tiles_deterministic(lib):
+    """The last arriver adds the K slices in slice order, so repeated calls
+    agree bit for bit whatever order the workgroups finish in."""
     p = inputs.draw_problems(5300, [(512, 512, 16384)])[0]
     runs = [run_gemm(lib, p) for _ in range(3)]
     assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
@@ -306,12 +307,13 @@ def test_group_small_m_panel(lib):
         assert_parity(got, c16, bound, "panel group %d" % i)
 
 
-def test_group_stream_k_mixed(lib):
-    """A stream-K grouped launch with ragged M and N, different K per group,
-    a K = 0 group (zero C) and an empty group."""
+def test_group_few_tiles_mixed(lib):
+    """A grouped launch with few 128 x 128 tiles on the 64-row kernels: ragged
+    M and N above 64, different K per group, a K = 0 group (zero C) and an
+    empty group."""
     shapes = [(300, 400, 8192), (129, 257, 16384), (200, 100, 0), (0, 64, 256), (256, 384, 8192), (65, 700, 6144)]
     info, _ = lib.group_gemm_plan(shapes)
-    assert info["kernel"] == 4
+    assert info["tile_m"] == 64 and info["split_k"] > 1
     probs = inputs.draw_problems(39, shapes)
     outs = run_group(lib, probs)
     for i, (p, got) in enumerate(zip(probs, outs)):
@@ -321,7 +323,7 @@ def test_group_stream_k_mixed(lib):
             assert np.all(got == 0)
             continue
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
-        assert_parity(got, c16, bound, "stream-K group %d" % i)
+        assert_parity(got, c16, bound, "few-tiles group %d" % i)
 
 
 def test_group_single_group_matches_gemm(lib):
