@@ -332,15 +332,12 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
     info->workspace_bytes = plan.workspace_bytes;
 }
 
-nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream, bool pow2 = false)
+// Launches a finished plan: groups in plan order, kMaxGroupsPerLaunch per
+// launch.
+nvfp4_status run_plan(const nvfp4_problem *problems, const Plan &plan, hipStream_t stream)
 {
-    Plan plan;
-    nvfp4_status s = make_plan(problems, num_groups, &plan, pow2);
-    if (s != NVFP4_OK || plan.total_tiles == 0)
-        return s;
-
     void *workspace = nullptr;
-    s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
+    nvfp4_status s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
     if (s != NVFP4_OK)
         return s;
 
@@ -384,6 +381,15 @@ nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stre
     return flush();
 }
 
+nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream, bool pow2 = false)
+{
+    Plan plan;
+    nvfp4_status s = make_plan(problems, num_groups, &plan, pow2);
+    if (s != NVFP4_OK || plan.total_tiles == 0)
+        return s;
+    return run_plan(problems, plan, stream);
+}
+
 // ---------------------------------------------------------------- blocked scales
 
 nvfp4_status check_scale_matrix(const void *a, const void *b, int rows, int K, const void *blocked)
@@ -420,9 +426,11 @@ nvfp4_status convert_one(const void *src, void *dst, int rows, int K, bool to_bl
     return nvfp4::launch_scale_conversion(t, stream) == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
 }
 
-// Grouped product with blocked scales: the scales are converted to the plain
-// layout in the stream's workspace (after the tile counters and whatever the
-// plan's K split needs), then the plain path runs on the converted copies.
+// Grouped product with blocked scales.  Where the plan takes one-wave 128 x
+// 128 tiles and every K is a multiple of 128, that kernel reads the blocked
+// scales directly.  Otherwise the scales are converted to the plain layout in
+// the stream's workspace (after the tile counters and whatever the plan's K
+// split needs), then the plain path runs on the converted copies.
 nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
 {
     Plan plan;
@@ -436,6 +444,14 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
     }
     if (plan.total_tiles == 0)
         return NVFP4_OK;
+    bool direct = plan.cfg == nvfp4::kTile128x128;
+    for (int g = 0; g < num_groups; ++g)
+        if (!empty_output(problems[g]) && problems[g].K % 128 != 0)
+            direct = false;
+    if (direct) {
+        plan.cfg = nvfp4::kTile128x128Blocked;
+        return run_plan(problems, plan, stream);
+    }
     auto up = [](long long x) { return (x + 255) & ~255LL; };
     const long long base = up(std::max<long long>(plan.workspace_bytes, nvfp4::kCounterBytes));
     std::vector<long long> off_a(num_groups, 0), off_b(num_groups, 0);

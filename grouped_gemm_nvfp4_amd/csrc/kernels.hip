@@ -943,6 +943,15 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 // of every row, 32 real K per 32x32 MFMA (the fp16 path needs two MFMAs and
 // eight decode instructions per fragment for the same 32 K).  Other scale
 // codes are outside this path's contract (their mantissa bits are ignored).
+//
+// kBlocked: SFA and SFB arrive in the blocked layout the pages' kernels
+// consume (512-byte atoms of 128 rows x 4 scale blocks, atoms of a 128-row
+// tile in K order; row r, block c of an atom at (r % 32) * 16 + (r / 32) * 4 +
+// c).  A 128 x 128 tile's scales for one 128-K tile are then its two
+// consecutive atoms, 1 KiB, one 16-byte direct load per lane per operand,
+// kept in LDS as they are; the compute reads row 32 i + l32's four blocks of
+// 64-K group g at 512 g + 16 l32 + 4 i.  Rows past M or N are the layout's
+// zero padding.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -962,9 +971,10 @@ __device__ inline void mfma_pow2_step(f32x16 (&acc)[4][4], const i32x8 (&fa)[4],
 
 // The work of one workgroup (one 128 x 128 tile); Table is the by-value
 // GroupTable of an ordinary launch or a DevTableView of a device-resident one.
-template <bool kPow2, class Table>
+template <bool kPow2, bool kBlocked, class Table>
 __device__ inline void tiled_dma_tile(const Table &tab, const int w)
 {
+    static_assert(!(kPow2 && kBlocked), "the power-of-two path reads plain scales");
     using namespace tiled;
     __shared__ __attribute__((aligned(16))) uint8_t stages[2 * kStageBytes];
     uint8_t *const stage0 = stages;
@@ -987,8 +997,14 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     const int nkt = K / BK;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
-    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
+    // blocked scales: one 128-row tile's atoms, K / 64 of them (K % 128 == 0)
+    const long atoms_bytes = (long)(K / 64) * 512;
+    const __amdgpu_buffer_rsrc_t rSA =
+        kBlocked ? make_rsrc(d.SFA + (long)tm * atoms_bytes, (uint64_t)atoms_bytes)
+                 : make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB =
+        kBlocked ? make_rsrc(d.SFB + (long)tn * atoms_bytes, (uint64_t)atoms_bytes)
+                 : make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
 
     // data: instruction j covers rows 16 j .. 16 j + 15
     const int drow = lane >> 2;
@@ -1006,13 +1022,21 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(st + kAOff + 1024 * j), 16, off, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(st + kBOff + 1024 * j), 16, off, 0, 0, 0);
         }
+        if (kBlocked) {
+            // the tile's two atoms of this K tile: 1 KiB per operand
+            const uint32_t off = live ? (uint32_t)kt * 1024 + (uint32_t)(lane * 16) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff), 16, off, 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t off = live ? s_off + (uint32_t)(32 * j * ks_row) + ks : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff + 256 * j), 4, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff + 256 * j), 4, off, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t off = live ? s_off + (uint32_t)(32 * j * ks_row) + ks : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff + 256 * j), 4, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff + 256 * j), 4, off, 0, 0, 0);
+            }
         }
     };
+
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -1033,10 +1057,18 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
         for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
-                const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
-                ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
-                cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
+                if constexpr (kBlocked) {
+                    // blocks 4 g .. 4 g + 3 of row 32 i + l32: word i of the row's 16 bytes in atom g
+                    const uint32_t wa = *(const uint32_t *)(st + kSaOff + 512 * g + 16 * l32 + 4 * i);
+                    const uint32_t wb = *(const uint32_t *)(st + kSbOff + 512 * g + 16 * l32 + 4 * i);
+                    ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa >> sh, 1.0f, false);
+                    cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb >> sh, 1.0f, false);
+                } else {
+                    const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
+                    const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
+                    ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
+                    cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
+                }
                 pa[g][i] = *(const u32x4 *)(st + kAOff + swz(32 * i + l32, 2 * g + h));
                 pb[g][i] = *(const u32x4 *)(st + kBOff + swz(32 * i + l32, 2 * g + h));
             }
@@ -1115,7 +1147,7 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     // at most the other stage's kIssued loads may still be in flight
     // (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
     // lgkmcnt 11:8 left at their maxima).
-    constexpr int kIssued = 8 + 8 + 4 + 4;
+    constexpr int kIssued = 8 + 8 + (kBlocked ? 2 : 8);
     constexpr int kWaitOther = ((kIssued >> 4) << 14) | (15 << 8) | (7 << 4) | (kIssued & 15);
     if (nkt > 0) {
         issue(stage0, 0);
@@ -1181,10 +1213,10 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     }
 }
 
-template <bool kPow2>
+template <bool kPow2, bool kBlocked>
 __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
 {
-    tiled_dma_tile<kPow2>(tab, (int)blockIdx.x);
+    tiled_dma_tile<kPow2, kBlocked>(tab, (int)blockIdx.x);
 }
 
 // Device-resident grouped launch: the table the plan kernel left in the
@@ -1196,7 +1228,7 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_dev_kernel(const uint8_t *w
         return;
     const DevTableView view = {hd.num_groups, (const int *)(ws + 16),
                                (const GemmDesc *)(ws + dev_desc_offset(hd.num_groups))};
-    tiled_dma_tile<false>(view, (int)blockIdx.x);
+    tiled_dma_tile<false, false>(view, (int)blockIdx.x);
 }
 
 // Plan of a device-resident grouped call, one workgroup: each thread checks
@@ -1399,6 +1431,7 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
     }
     case kTile128x128K4:
     case kTile128x128Pow2:
+    case kTile128x128Blocked:
     case kTile128x128:
     default: {
         bool vec = true;
@@ -1406,15 +1439,26 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             vec = vec && (table.g[g].K % tiled::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 7) == 0;
         const bool four = cfg == kTile128x128K4;
+        if (cfg == kTile128x128Blocked) {
+            // blocked scales move in 16-byte pieces: 16-byte aligned arrays
+            bool ok = true;
+            for (int g = 0; g < table.num_groups; ++g)
+                ok = ok && (table.g[g].K % tiled::BK) == 0 &&
+                     ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
+            if (!ok)
+                return hipErrorInvalidValue;
+            void *dargs[] = {const_cast<GroupTable *>(&table)};
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false, true>, dim3(tiles), dim3(64), dargs, 0, stream);
+        }
         if (cfg == kTile128x128Pow2) {
             if (!vec)
                 return hipErrorInvalidValue;
             void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true>, dim3(tiles), dim3(64), dargs, 0, stream);
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true, false>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
         if (!four && vec) {
             void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false>, dim3(tiles), dim3(64), dargs, 0, stream);
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false, false>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
                               : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);

@@ -72,6 +72,7 @@ enum TileConfig : int {
     kTile128x128K4 = 2, // 128 x 128 tile, four waves splitting its K, sums added in LDS
     kPanel64x64 = 3,    // 8 waves split K, each owning the 64 x 64 tile; K may be split
     kTile128x128Pow2 = 5, // one-wave 128 x 128 tiles on the scaled FP4 MFMA (power-of-two scales)
+    kTile128x128Blocked = 6, // one-wave 128 x 128 direct-to-LDS tiles, scales in the blocked layout
 };
 
 struct TileShape {
@@ -87,6 +88,7 @@ inline TileShape tile_shape(TileConfig c)
         return {64, 64, 256};
     case kTile128x128K4:
     case kTile128x128Pow2:
+    case kTile128x128Blocked:
     case kTile128x128:
     default:
         return {128, 128, 128};

@@ -172,12 +172,15 @@ nvfp4_status nvfp4_scales_from_blocked(const void *blocked, void *sf, int rows, 
                                        hipStream_t stream);
 
 /* nvfp4_gemm / nvfp4_group_gemm with SFA and SFB in the blocked layout
- * (16-byte aligned, nvfp4_blocked_scale_bytes(M or N, K) bytes each).  The
- * scales are first converted to the plain layout inside the library's
- * per-stream device workspace (so the call may allocate it, and returns
- * NOT_SUPPORTED inside a stream capture if it would have to); then the plain
- * path runs, so C is bitwise what nvfp4_gemm gives for the same scales.
- * Other arguments, limits and errors as for the plain entry points. */
+ * (16-byte aligned, nvfp4_blocked_scale_bytes(M or N, K) bytes each).  Where
+ * the plain call would run one-wave 128 x 128 tiles and every K is a multiple
+ * of 128 (large and grouped products), that kernel reads the blocked scales
+ * directly.  Otherwise the scales are first converted to the plain layout
+ * inside the library's per-stream device workspace (so the call may allocate
+ * it, and returns NOT_SUPPORTED inside a stream capture if it would have to)
+ * and the plain path runs.  Either way C is bitwise what nvfp4_gemm gives for
+ * the same scales.  Other arguments, limits and errors as for the plain entry
+ * points. */
 nvfp4_status nvfp4_gemm_blocked(const void *A, const void *SFA, const void *B, const void *SFB,
                                 void *C, int M, int N, int K, hipStream_t stream);
 nvfp4_status nvfp4_group_gemm_blocked(const nvfp4_problem *problems, int num_groups,

@@ -388,7 +388,7 @@ def blocked_dev(sf, rows, K):
 @pytest.mark.parametrize("M,N,K", [
     (64, 6144, 8192),    # panel kernel with a K split (tile counters in the workspace)
     (40, 500, 1024),     # stream kernel
-    (300, 260, 2080),    # tiled kernel, ragged K tile
+    (300, 260, 2080),    # few tiles with M > 64, ragged K tile: converted scales
 ])
 def test_gemm_blocked_equals_plain(lib, M, N, K):
     p = inputs.draw_problems(5400 + M + K, [(M, N, K)])[0]
@@ -402,6 +402,50 @@ def test_gemm_blocked_equals_plain(lib, M, N, K):
     assert np.array_equal(bits(C2), plain)
     c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
     assert_parity(plain, c16, bound, "blocked %dx%dx%d" % (M, N, K))
+
+
+def test_gemm_blocked_direct_equals_plain(lib):
+    """306 one-wave 128 x 128 tiles with ragged M and N: the kernel reads the
+    blocked scales directly (two atoms per K tile), padding rows included, and
+    gives bitwise the plain call's C."""
+    M, N, K = 2300, 2170, 1024
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == 1 and info["tile_m"] == 128
+    p = inputs.draw_problems(5450, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    plain = bits(C)
+    C2 = poisoned(M, N)
+    lib.nvfp4_gemm_blocked(A, blocked_dev(p.SFA, M, K), B, blocked_dev(p.SFB, N, K), C2, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(C2), plain)
+    check_sampled(plain, p, 5451, "blocked direct %dx%dx%d" % (M, N, K))
+
+
+def test_group_gemm_blocked_direct(lib):
+    """A grouped call on one-wave 128 x 128 tiles (448 tiles, K 256 to 1024,
+    an empty group and a K = 0 group) with blocked scales read directly:
+    bitwise the plain grouped call, sampled against the oracle."""
+    shapes = [(1000, 4096, 512), (300, 4096, 1024), (64, 4096, 256), (0, 64, 256), (130, 4096, 0)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["kernel"] == 1 and info["tile_m"] == 128
+    probs = inputs.draw_problems(43, shapes)
+    plain = run_group(lib, probs)
+    devs = [dev_problem(p) for p in probs]
+    lib.nvfp4_group_gemm_blocked([(d[0], blocked_dev(p.SFA, p.M, p.K) if p.K else d[1], d[2],
+                                   blocked_dev(p.SFB, p.N, p.K) if p.K else d[3], d[4], p.M, p.N, p.K)
+                                  for d, p in zip(devs, probs)])
+    torch.cuda.synchronize()
+    for i, (d, p) in enumerate(zip(devs, probs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        got = bits(d[4])
+        assert np.array_equal(got, plain[i]), "blocked group %d differs from the plain call" % i
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        check_sampled(got, p, 44 + i, "blocked direct group %d" % i)
 
 
 def test_group_gemm_blocked_then_plain_split(lib):
