@@ -944,7 +944,14 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 // eight decode instructions per fragment for the same 32 K).  Other scale
 // codes are outside this path's contract (their mantissa bits are ignored).
 //
-// kBlocked: SFA and SFB arrive in the blocked layout the pages' kernels
+// kScales, how the scales reach LDS.  kScalesPlain: [rows][K/16] scales, four
+// 4-byte loads per lane per operand and K tile (8 bytes from each of 32 rows
+// per instruction).  kScalesPairs (every K % 256 == 0): [rows][K/16] scales of
+// two K tiles at once, one 16-byte load per lane and 64 rows (a row's 8 + 8
+// bytes are adjacent), into one of two pair buffers (rows of 16 bytes; tile
+// kt's 8 bytes at 8 (kt % 2)), half the instructions and half the cache lines
+// per K tile.  The pair buffers reuse the stages' scale areas plus 4 KiB.
+// kScalesBlocked: SFA and SFB arrive in the blocked layout the pages' kernels
 // consume (512-byte atoms of 128 rows x 4 scale blocks, atoms of a 128-row
 // tile in K order; row r, block c of an atom at (r % 32) * 16 + (r / 32) * 4 +
 // c).  A 128 x 128 tile's scales for one 128-K tile are then its two
@@ -954,6 +961,7 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 // zero padding.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kScalesPlain = 0, kScalesPairs = 1, kScalesBlocked = 2;
 
 // The 16 MFMAs of one power-of-two step: the scale bytes sit in byte kSel of
 // each lane's exponent dwords.
@@ -971,14 +979,19 @@ __device__ inline void mfma_pow2_step(f32x16 (&acc)[4][4], const i32x8 (&fa)[4],
 
 // The work of one workgroup (one 128 x 128 tile); Table is the by-value
 // GroupTable of an ordinary launch or a DevTableView of a device-resident one.
-template <bool kPow2, bool kBlocked, class Table>
+template <bool kPow2, int kScales, class Table>
 __device__ inline void tiled_dma_tile(const Table &tab, const int w)
 {
-    static_assert(!(kPow2 && kBlocked), "the power-of-two path reads plain scales");
+    constexpr bool kBlocked = kScales == kScalesBlocked;
+    constexpr bool kPairs = kScales == kScalesPairs;
+    static_assert(!kPow2 || kScales == kScalesPlain, "the power-of-two path reads plain scales");
     using namespace tiled;
-    __shared__ __attribute__((aligned(16))) uint8_t stages[2 * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t stages[2 * kStageBytes + (kPairs ? 4096 : 0)];
     uint8_t *const stage0 = stages;
     uint8_t *const stage1 = stages + kStageBytes;
+    // pair buffers (kPairs): A's in the stages' 2 KiB scale areas, B's past them
+    auto qa = [&](int q) { return stages + q * kStageBytes + kSaOff; };
+    auto qb = [&](int q) { return stages + 2 * kStageBytes + 2048 * q; };
 
     const int gi = find_group(tab, w);
     const GemmDesc &d = tab.g[gi];
@@ -1022,7 +1035,9 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(st + kAOff + 1024 * j), 16, off, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(st + kBOff + 1024 * j), 16, off, 0, 0, 0);
         }
-        if (kBlocked) {
+        if (kPairs) {
+            // scales move in pairs of K tiles (issue_pair)
+        } else if (kBlocked) {
             // the tile's two atoms of this K tile: 1 KiB per operand
             const uint32_t off = live ? (uint32_t)kt * 1024 + (uint32_t)(lane * 16) : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff), 16, off, 0, 0, 0);
@@ -1034,6 +1049,17 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff + 256 * j), 4, off, 0, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff + 256 * j), 4, off, 0, 0, 0);
             }
+        }
+    };
+    // scales of K tiles kt and kt + 1 (kt even) into pair buffer q: instruction
+    // j covers rows 64 j .. 64 j + 63, lane i row 64 j + i
+    auto issue_pair = [&](int q, int kt) {
+        const bool live = kt < nkt;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t off = live ? (uint32_t)((64 * j + lane) * ks_row + kt * kSfBytes) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(qa(q) + 1024 * j), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(qb(q) + 1024 * j), 16, off, 0, 0, 0);
         }
     };
 
@@ -1050,14 +1076,21 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     // first decode step, then every MFMA followed by the next step's decode
     // VALU (4 per MFMA, 5 across the group boundary, where the second
     // group's scales and first step are decoded), then the last step's MFMAs.
-    auto compute = [&](const uint8_t *st) {
+    // (kPairs: the scales come from pair buffer q, tile half `half`)
+    auto compute = [&](const uint8_t *st, int q, int half) {
         half2_t ca[2][4], cb[2][4];
         u32x4 pa[2][4], pb[2][4];
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (kBlocked) {
+                if constexpr (kPairs) {
+                    const int o = (32 * i + l32) * 16 + 8 * half + 4 * g;
+                    const uint32_t wa = *(const uint32_t *)(qa(q) + o);
+                    const uint32_t wb = *(const uint32_t *)(qb(q) + o);
+                    ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa >> sh, 1.0f, false);
+                    cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb >> sh, 1.0f, false);
+                } else if constexpr (kBlocked) {
                     // blocks 4 g .. 4 g + 3 of row 32 i + l32: word i of the row's 16 bytes in atom g
                     const uint32_t wa = *(const uint32_t *)(st + kSaOff + 512 * g + 16 * l32 + 4 * i);
                     const uint32_t wb = *(const uint32_t *)(st + kSbOff + 512 * g + 16 * l32 + 4 * i);
@@ -1147,9 +1180,30 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     // at most the other stage's kIssued loads may still be in flight
     // (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
     // lgkmcnt 11:8 left at their maxima).
-    constexpr int kIssued = 8 + 8 + (kBlocked ? 2 : 8);
+    constexpr int kIssued = 8 + 8 + (kPairs ? 4 : kBlocked ? 2 : 8);
     constexpr int kWaitOther = ((kIssued >> 4) << 14) | (15 << 8) | (7 << 4) | (kIssued & 15);
-    if (nkt > 0) {
+    if (kPairs && nkt > 0) {
+        // stage data as below; scale pairs one iteration ahead.  Before each
+        // compute, this iteration's data (16) and next pair (4), or next data
+        // stage, may still be in flight: every wait leaves kIssued.
+        issue(stage0, 0);
+        issue_pair(0, 0);
+        for (int kt = 0, q = 0; kt < nkt; kt += 2, q ^= 1) {
+            issue(stage1, kt + 1);
+            issue_pair(q ^ 1, kt + 2);
+            SCHED_FENCE();
+            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage0 and pair q have landed
+            SCHED_FENCE();
+            compute(stage0, q, 0);
+            SCHED_FENCE();
+            issue(stage0, kt + 2);
+            SCHED_FENCE();
+            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage1 has landed
+            SCHED_FENCE();
+            compute(stage1, q, 1);
+            SCHED_FENCE();
+        }
+    } else if (nkt > 0) {
         issue(stage0, 0);
         for (int kt = 0; kt < nkt; kt += 2) {
             issue(stage1, kt + 1);
@@ -1159,7 +1213,7 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
             if (kPow2)
                 compute_pow2(stage0);
             else
-                compute(stage0);
+                compute(stage0, 0, 0);
             SCHED_FENCE();
             issue(stage0, kt + 2);
             SCHED_FENCE();
@@ -1170,7 +1224,7 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
             if (kPow2)
                 compute_pow2(stage1);
             else
-                compute(stage1);
+                compute(stage1, 0, 0);
             SCHED_FENCE();
         }
     }
@@ -1213,10 +1267,10 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     }
 }
 
-template <bool kPow2, bool kBlocked>
+template <bool kPow2, int kScales>
 __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
 {
-    tiled_dma_tile<kPow2, kBlocked>(tab, (int)blockIdx.x);
+    tiled_dma_tile<kPow2, kScales>(tab, (int)blockIdx.x);
 }
 
 // Device-resident grouped launch: the table the plan kernel left in the
@@ -1228,7 +1282,7 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_dev_kernel(const uint8_t *w
         return;
     const DevTableView view = {hd.num_groups, (const int *)(ws + 16),
                                (const GemmDesc *)(ws + dev_desc_offset(hd.num_groups))};
-    tiled_dma_tile<false, false>(view, (int)blockIdx.x);
+    tiled_dma_tile<false, kScalesPlain>(view, (int)blockIdx.x);
 }
 
 // Plan of a device-resident grouped call, one workgroup: each thread checks
@@ -1448,17 +1502,22 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             if (!ok)
                 return hipErrorInvalidValue;
             void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false, true>, dim3(tiles), dim3(64), dargs, 0, stream);
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false, kScalesBlocked>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
         if (cfg == kTile128x128Pow2) {
             if (!vec)
                 return hipErrorInvalidValue;
             void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true, false>, dim3(tiles), dim3(64), dargs, 0, stream);
+            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true, kScalesPlain>, dim3(tiles), dim3(64), dargs, 0, stream);
         }
         if (!four && vec) {
+            bool pairs = true; // even K tile counts: scales in pairs of K tiles
+            for (int g = 0; g < table.num_groups; ++g)
+                pairs = pairs && (table.g[g].K % (2 * tiled::BK)) == 0;
             void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false, false>, dim3(tiles), dim3(64), dargs, 0, stream);
+            const void *fn = pairs ? (const void *)gemm_tiled_dma_kernel<false, kScalesPairs>
+                                   : (const void *)gemm_tiled_dma_kernel<false, kScalesPlain>;
+            return hipLaunchKernel(fn, dim3(tiles), dim3(64), dargs, 0, stream);
         }
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
                               : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);

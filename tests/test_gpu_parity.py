@@ -126,6 +126,20 @@ def test_tiled_variants(lib, M, N, K, kernel):
         check_sampled(got, p, 91, "tiled %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (2300, 2170, 1024),  # K % 256 == 0: scales of two K tiles per load
+    (2300, 2170, 1152),  # odd K tile count: per-K-tile scale loads
+])
+def test_one_wave_tiles_scale_loads(lib, M, N, K):
+    """306 ragged one-wave 128 x 128 tiles, with each of the two ways the
+    direct-to-LDS kernel fetches plain scales."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == 1 and info["tile_m"] == 128
+    p = inputs.draw_problems(4100 + K, [(M, N, K)])[0]
+    got = run_gemm(lib, p)
+    check_sampled(got, p, 4101 + K, "one-wave %dx%dx%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("M,N,K,split", [
     (64, 6144, 8192, 2),    # scale groups of four K tiles, K split in two
     (64, 16384, 4096, 1),   # no split
