@@ -151,7 +151,20 @@ def cpu_baseline(probs, target_s):
         sample = ("leading %s rows of M (all N and K) of each problem: %.3g of the "
                   "workload's flops, %.1f s" % (rows, done / total_flops, dt))
     return {"value": done / dt / 1e12, "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():

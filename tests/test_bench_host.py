@@ -38,3 +38,4 @@ def test_cpu_baseline_reports_the_oracle():
     assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOPS"
     assert cpu["value"] > 0 and cpu["cores"] >= 1
     assert "workload" in cpu["sample"] or "rows" in cpu["sample"]
+    assert "cpu_model" in cpu and "omp_num_threads" in cpu
