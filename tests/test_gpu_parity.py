@@ -188,6 +188,34 @@ def test_few_tiles_take_64_row_kernels(lib, M, N, K):
     check_full(lib, p, "few tiles %dx%dx%d split %d" % (M, N, K, info["split_k"]))
 
 
+def _random_regime_shapes():
+    rng = np.random.default_rng(2024)
+    shapes = []
+    for regime in range(4):
+        for _ in range(2):
+            if regime == 0:    # M <= 64
+                shapes.append((int(rng.integers(1, 65)), int(rng.integers(1, 9000)), 32 * int(rng.integers(1, 400))))
+            elif regime == 1:  # M > 64, few 128 x 128 tiles: 64-row kernels
+                shapes.append((int(rng.integers(65, 1600)), int(rng.integers(1, 1600)), 32 * int(rng.integers(1, 300))))
+            elif regime == 2:  # many tiles, K % 128 == 0
+                shapes.append((int(rng.integers(1000, 4200)), int(rng.integers(1000, 4200)), 128 * int(rng.integers(1, 24))))
+            else:              # many tiles, K % 256 == 0 (scales two K tiles per load)
+                shapes.append((int(rng.integers(1500, 3500)), int(rng.integers(1500, 3500)), 256 * int(rng.integers(1, 12))))
+    return shapes
+
+
+@pytest.mark.parametrize("M,N,K", _random_regime_shapes())
+def test_random_shapes_across_planner_regimes(lib, M, N, K):
+    """Seeded random shapes in each of the planner's regimes; outputs checked
+    in full where the oracle is quick, else sampled (edge rows and columns
+    included), and never left unwritten."""
+    p = inputs.draw_problems(9100 + M + K, [(M, N, K)])[0]
+    if M * N <= 300_000:
+        check_full(lib, p, "random %dx%dx%d" % (M, N, K))
+    else:
+        check_sampled(run_gemm(lib, p), p, 9101 + N, "random %dx%dx%d" % (M, N, K))
+
+
 def test_few_tiles_deterministic(lib):
     """The last arriver adds the K slices in slice order, so repeated calls
     agree bit for bit whatever order the workgroups finish in."""
