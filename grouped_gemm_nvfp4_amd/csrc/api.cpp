@@ -153,13 +153,13 @@ constexpr int kMaxSplitK = 16;
 // on 64x7168x16384, 1x7168x16384, 64x16384x4096).
 constexpr int kPanelMinWorkgroups = 192;
 // Launches of M > 64 with at most this many 128 x 128 tiles also take the
-// 64-row kernels.  Measured (event means, us; 64-row route vs the one-, four-
-// wave or stream-K 128 x 128 route it replaces): 128x128x256 4.9 vs 14.2,
-// 1024x1024x4096 16.2 vs 45.2, 512x512x16384 19.5 vs 83.7, 129x257x32768 19.5
-// vs 107.7, 512x4096x7168 45.7 vs 67.1, 2048x1536x4096 (192 tiles) 46.7 vs
-// 51.6; but 1792x2048x4096 (224 tiles) 61.4 vs 52.3 and 2048x2048x4096 60.2 vs
-// 52.8.
-constexpr long long kPanelMaxTiles128 = 192;
+// 64-row kernels.  Measured (event means, us; 64-row route vs the one-wave or
+// four-wave 128 x 128 route): 128x128x256 4.9 vs 14.2, 1024x1024x4096 16.4
+// vs 35.5, 512x512x16384 18.6 vs 88.3, 512x4096x7168 46.0 vs 55.7,
+// 1024x2048x16384 79.8 vs 105.3, 2048x1024x2048 23.2 vs 26.6 (128 tiles); but
+// 2048x1280x4096 (160 tiles) 44.6 vs 39.8 and 2048x1536x4096 (192) 47.5 vs
+// 42.4, where the four-wave form takes over.
+constexpr long long kPanelMaxTiles128 = 128;
 
 // Output tiles of every group under tile shape ts (prefix[g + 1] is the
 // running total) and the longest K in K tiles.

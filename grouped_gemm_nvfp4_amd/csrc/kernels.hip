@@ -979,14 +979,26 @@ __device__ inline void mfma_pow2_step(f32x16 (&acc)[4][4], const i32x8 (&fa)[4],
 
 // The work of one workgroup (one 128 x 128 tile); Table is the by-value
 // GroupTable of an ordinary launch or a DevTableView of a device-resident one.
-template <bool kPow2, int kScales, class Table>
+//
+// kWaves = 4: four waves share the tile, each running the pipeline above over
+// a quarter of its K tiles (whole pairs of K tiles with paired scales) in an
+// LDS region of its own (the four regions fill the CU's 160 KiB), with no
+// barrier in the K loop.  Their partial tiles are then added through LDS in a
+// fixed order, (w0 + w2) + (w1 + w3), and wave 0 writes C.  One workgroup per
+// CU: used where tiles are too few for one wave per tile to fill the SIMDs.
+template <bool kPow2, int kScales, int kWaves, class Table>
 __device__ inline void tiled_dma_tile(const Table &tab, const int w)
 {
     constexpr bool kBlocked = kScales == kScalesBlocked;
     constexpr bool kPairs = kScales == kScalesPairs;
     static_assert(!kPow2 || kScales == kScalesPlain, "the power-of-two path reads plain scales");
+    static_assert(kWaves == 1 || (!kPow2 && !kBlocked), "four-wave tiles read plain scales");
     using namespace tiled;
-    __shared__ __attribute__((aligned(16))) uint8_t stages[2 * kStageBytes + (kPairs ? 4096 : 0)];
+    constexpr int kWaveLds = 2 * kStageBytes + (kPairs ? 4096 : 0);
+    static_assert(kWaves * kWaveLds <= 160 * 1024, "the wave regions fit in LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t stages_all[kWaves * kWaveLds];
+    const int wv = kWaves > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+    uint8_t *const stages = kWaves == 1 ? stages_all : stages_all + wv * kWaveLds;
     uint8_t *const stage0 = stages;
     uint8_t *const stage1 = stages + kStageBytes;
     // pair buffers (kPairs): A's in the stages' 2 KiB scale areas, B's past them
@@ -1008,6 +1020,10 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     const int kb_row = K / 2;
     const int ks_row = K / 16;
     const int nkt = K / BK;
+    // this wave's K tiles [kt_lo, kt_hi): all of them, or a quarter (whole
+    // pairs of K tiles when the scales move in pairs)
+    const int kt_lo = kWaves == 1 ? 0 : kPairs ? 2 * ((nkt / 2) * wv / kWaves) : nkt * wv / kWaves;
+    const int kt_hi = kWaves == 1 ? nkt : kPairs ? 2 * ((nkt / 2) * (wv + 1) / kWaves) : nkt * (wv + 1) / kWaves;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
     // blocked scales: one 128-row tile's atoms, K / 64 of them (K % 128 == 0)
@@ -1025,9 +1041,9 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     // scales: instruction j covers rows 32 j .. 32 j + 31 (two dwords each)
     const uint32_t s_off = (uint32_t)((lane >> 1) * ks_row + (lane & 1) * 4);
 
-    // tile kt into stage `st` (tiles past nkt read as zero)
+    // tile kt into stage `st` (tiles past kt_hi read as zero)
     auto issue = [&](uint8_t *st, int kt) {
-        const bool live = kt < nkt;
+        const bool live = kt < kt_hi;
         const uint32_t kb = (uint32_t)kt * kRowBytes, ks = (uint32_t)kt * kSfBytes;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1054,7 +1070,7 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     // scales of K tiles kt and kt + 1 (kt even) into pair buffer q: instruction
     // j covers rows 64 j .. 64 j + 63, lane i row 64 j + i
     auto issue_pair = [&](int q, int kt) {
-        const bool live = kt < nkt;
+        const bool live = kt < kt_hi;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t off = live ? (uint32_t)((64 * j + lane) * ks_row + kt * kSfBytes) : kOutOfRange;
@@ -1182,13 +1198,13 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
     // lgkmcnt 11:8 left at their maxima).
     constexpr int kIssued = 8 + 8 + (kPairs ? 4 : kBlocked ? 2 : 8);
     constexpr int kWaitOther = ((kIssued >> 4) << 14) | (15 << 8) | (7 << 4) | (kIssued & 15);
-    if (kPairs && nkt > 0) {
+    if (kPairs && kt_hi > kt_lo) {
         // stage data as below; scale pairs one iteration ahead.  Before each
         // compute, this iteration's data (16) and next pair (4), or next data
         // stage, may still be in flight: every wait leaves kIssued.
-        issue(stage0, 0);
-        issue_pair(0, 0);
-        for (int kt = 0, q = 0; kt < nkt; kt += 2, q ^= 1) {
+        issue(stage0, kt_lo);
+        issue_pair(0, kt_lo);
+        for (int kt = kt_lo, q = 0; kt < kt_hi; kt += 2, q ^= 1) {
             issue(stage1, kt + 1);
             issue_pair(q ^ 1, kt + 2);
             SCHED_FENCE();
@@ -1203,9 +1219,9 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
             compute(stage1, q, 1);
             SCHED_FENCE();
         }
-    } else if (nkt > 0) {
-        issue(stage0, 0);
-        for (int kt = 0; kt < nkt; kt += 2) {
+    } else if (kt_hi > kt_lo) {
+        issue(stage0, kt_lo);
+        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
             issue(stage1, kt + 1);
             SCHED_FENCE();
             __builtin_amdgcn_s_waitcnt(kWaitOther); // stage0 has landed
@@ -1227,6 +1243,50 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
                 compute(stage1, 0, 0);
             SCHED_FENCE();
         }
+    }
+
+    if constexpr (kWaves > 1) {
+        // add the four partial tiles: 16-byte pieces (i, j, e / 4) of each
+        // lane, [piece][lane], in slots of 64 KiB over the whole LDS
+        __builtin_amdgcn_s_waitcnt(0); // this wave's trailing zero loads have landed
+        __syncthreads();               // every wave is past its K loop
+        float *red = (float *)stages_all;
+        auto put = [&](int slot) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        *(float4 *)(red + slot * 16384 + (((i * 4 + j) * 4 + e) * 64 + lane) * 4) =
+                            (float4){acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]};
+        };
+        auto add = [&](int slot) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float4 v = *(const float4 *)(red + slot * 16384 + (((i * 4 + j) * 4 + e) * 64 + lane) * 4);
+                        acc[i][j][4 * e] += v.x;
+                        acc[i][j][4 * e + 1] += v.y;
+                        acc[i][j][4 * e + 2] += v.z;
+                        acc[i][j][4 * e + 3] += v.w;
+                    }
+        };
+        if (wv >= 2)
+            put(wv - 2);
+        __syncthreads();
+        if (wv < 2)
+            add(wv);
+        __syncthreads();
+        if (wv == 1)
+            put(0);
+        __syncthreads();
+        if (wv != 0)
+            return;
+        add(0);
     }
 
     // epilogue: fp16 (round to nearest even) rows 0..63 into stage0 and rows
@@ -1270,7 +1330,14 @@ __device__ inline void tiled_dma_tile(const Table &tab, const int w)
 template <bool kPow2, int kScales>
 __global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
 {
-    tiled_dma_tile<kPow2, kScales>(tab, (int)blockIdx.x);
+    tiled_dma_tile<kPow2, kScales, 1>(tab, (int)blockIdx.x);
+}
+
+// Four waves per 128 x 128 tile, each over a quarter of its K.
+template <int kScales>
+__global__ __launch_bounds__(256) void gemm_tiled_dma4_kernel(GroupTable tab)
+{
+    tiled_dma_tile<false, kScales, 4>(tab, (int)blockIdx.x);
 }
 
 // Device-resident grouped launch: the table the plan kernel left in the
@@ -1282,7 +1349,7 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_dev_kernel(const uint8_t *w
         return;
     const DevTableView view = {hd.num_groups, (const int *)(ws + 16),
                                (const GemmDesc *)(ws + dev_desc_offset(hd.num_groups))};
-    tiled_dma_tile<false, kScalesPlain>(view, (int)blockIdx.x);
+    tiled_dma_tile<false, kScalesPlain, 1>(view, (int)blockIdx.x);
 }
 
 // Plan of a device-resident grouped call, one workgroup: each thread checks
@@ -1518,6 +1585,15 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
             const void *fn = pairs ? (const void *)gemm_tiled_dma_kernel<false, kScalesPairs>
                                    : (const void *)gemm_tiled_dma_kernel<false, kScalesPlain>;
             return hipLaunchKernel(fn, dim3(tiles), dim3(64), dargs, 0, stream);
+        }
+        if (four && vec) {
+            bool pairs = true; // even K tile counts: scales in pairs of K tiles
+            for (int g = 0; g < table.num_groups; ++g)
+                pairs = pairs && (table.g[g].K % (2 * tiled::BK)) == 0;
+            void *dargs[] = {const_cast<GroupTable *>(&table)};
+            const void *fn = pairs ? (const void *)gemm_tiled_dma4_kernel<kScalesPairs>
+                                   : (const void *)gemm_tiled_dma4_kernel<kScalesPlain>;
+            return hipLaunchKernel(fn, dim3(tiles), dim3(256), dargs, 0, stream);
         }
         const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
                               : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);

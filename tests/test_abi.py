@@ -126,21 +126,21 @@ def test_plan_group_prefix_is_exclusive_scan_of_tile_counts():
 @pytest.mark.parametrize("M,N,K,tile_m", [
     (64, 7168, 16384, 64),     # M <= 64: 64-row kernels
     (128, 128, 256, 64),       # one 128 x 128 tile: 64-row kernels
-    (2048, 1536, 4096, 64),    # 192 tiles of 128 x 128: still the 64-row kernels
-    (2048, 1664, 4096, 128),   # 208 tiles: 128 x 128 tiles
+    (2048, 1024, 4096, 64),    # 128 tiles of 128 x 128: still the 64-row kernels
+    (2048, 1152, 4096, 128),   # 144 tiles: 128 x 128 tiles
     (8192, 8192, 8192, 128),   # 4096 tiles
 ])
 def test_plan_tile_rows_follow_the_128_tile_count(M, N, K, tile_m):
-    """Launches with M > 64 and at most 192 tiles of 128 x 128 take the 64-row
+    """Launches with M > 64 and at most 128 tiles of 128 x 128 take the 64-row
     kernels; larger ones take 128 x 128 tiles."""
     assert g.gemm_plan(M, N, K)["tile_m"] == tile_m
 
 
 def test_plan_group_tile_rows_count_all_groups():
-    """The 192-tile limit is on the whole launch: 6 groups of 32 tiles fit
-    under it, 7 do not."""
-    assert g.group_gemm_plan([(128, 4096, 1024)] * 6)[0]["tile_m"] == 64
-    assert g.group_gemm_plan([(128, 4096, 1024)] * 7)[0]["tile_m"] == 128
+    """The 128-tile limit is on the whole launch: 4 groups of 32 tiles fit
+    under it, 5 do not."""
+    assert g.group_gemm_plan([(128, 4096, 1024)] * 4)[0]["tile_m"] == 64
+    assert g.group_gemm_plan([(128, 4096, 1024)] * 5)[0]["tile_m"] == 128
 
 
 def test_plan_errors_match_call_errors():

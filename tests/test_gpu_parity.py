@@ -140,6 +140,24 @@ def test_one_wave_tiles_scale_loads(lib, M, N, K):
     check_sampled(got, p, 4101 + K, "one-wave %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (2048, 2048, 512),   # two of the four waves get no K tile (zero partial tiles)
+    (1700, 1900, 2048),  # ragged M and N, scales two K tiles per load
+    (2027, 1839, 1536),  # six pairs of K tiles: quarters of 1, 2, 1 and 2 pairs
+    (1800, 2000, 1152),  # odd K tile count: per-K-tile scale loads
+])
+def test_four_wave_direct_tiles(lib, M, N, K):
+    """The four-wave form of the direct-to-LDS 128 x 128 tile: each wave takes
+    a quarter of K in its own LDS region, the partial tiles are added through
+    LDS and wave 0 writes C."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == 3 and info["tile_m"] == 128
+    p = inputs.draw_problems(4200 + K, [(M, N, K)])[0]
+    got = run_gemm(lib, p)
+    check_sampled(got, p, 4201 + K, "four-wave %dx%dx%d" % (M, N, K))
+    assert np.array_equal(got, run_gemm(lib, p)), "four-wave sums must not depend on timing"
+
+
 @pytest.mark.parametrize("M,N,K,split", [
     (64, 6144, 8192, 2),    # scale groups of four K tiles, K split in two
     (64, 16384, 4096, 1),   # no split
@@ -180,7 +198,7 @@ def test_scale_pointers_at_odd_offsets(lib, M, N, K):
     (129, 257, 32768),   # mostly padding rows and columns, K split in sixteen
 ])
 def test_few_tiles_take_64_row_kernels(lib, M, N, K):
-    """M > 64 with at most 192 tiles of 128 x 128 runs on the 64-row kernels
+    """M > 64 with at most 128 tiles of 128 x 128 runs on the 64-row kernels
     (eight waves per workgroup, K split within and across workgroups)."""
     info = lib.gemm_plan(M, N, K)
     assert info["tile_m"] == 64
