@@ -19,7 +19,7 @@ timed region measured with HIP events on the launch stream, divided by the
 number of steps), and the CPU oracle's throughput on a bounded sample of the
 same workload.  The roofline's "traffic" (HBM bytes per launch from the
 FETCH_SIZE and WRITE_SIZE counters) comes from profiles/hbm_traffic.txt and is
-reported only while the kernel source it was measured on is unchanged.
+reported only while the kernel sources it was measured on are unchanged.
 
     python bench.py --copy-probe BYTES
 
@@ -78,17 +78,28 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "grouped_gemm_nvfp4_amd", "csrc", "kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "grouped_gemm_nvfp4_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def kernel_source_sha():
+    """sha256 over the device sources (csrc/*.hip and csrc/*.h, by name):
+    what the traffic figures are keyed to."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload):
     """HBM bytes per launch recorded for this workload, if they were measured
-    on the current kernel source (lines: workload sha256 bytes)."""
+    on the current kernel sources (lines: workload sha256 bytes)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(KERNEL_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = kernel_source_sha()
     with open(TRAFFIC_FILE) as f:
         for line in f:
             parts = line.split("#")[0].split()

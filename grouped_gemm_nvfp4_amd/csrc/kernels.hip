@@ -1,93 +1,14 @@
-// kernels.hip -- gfx950 (CDNA4) kernels for NVFP4 block-scaled GEMM.
-//
-// C[m][n] = fp16_rne( sum_k (A[m][k] * SFA[m][k/16]) * (B[n][k] * SFB[n][k/16]) )
-// (kernelbot pages nvfp4-group-gemm-498453 / nvfp4-gemm-125598, block-scaled MMA
-// loop; raw-CUDA page nvfp4-group-gemm-407526, round-to-nearest fp16 epilogue).
-//
-// Scale mapping onto CDNA4.  gfx950's scaled FP4 matrix instructions take one
-// power-of-two (e8m0) scale per 32 K elements, while NVFP4 carries a full e4m3
-// scale (4 significant bits) per 16.  Every element times its scale,
-// e2m1 * e4m3, has at most 6 significant bits and lies in [2^-10, 2688], so it
-// is exact in binary16; the product of two such values is exact in fp32.  The
-// kernels therefore decode each nibble to fp16 (v_cvt_scalef32_pk_f16_fp4 with
-// unit scale), multiply by the block's scale decoded to fp16
-// (v_cvt_scalef32_pk_f16_fp8, then v_pk_mul_f16: exact), and feed
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation.  Only the fp32 accumulation
-// rounds.  The scaled FP4/FP8 matrix instructions cannot carry the e4m3
-// mantissa without error, so they are not used.
-//
-// MFMA operand placement.  For v_mfma_f32_32x32x16_f16 lane l supplies 8 fp16
-// of A row (l % 32) and 8 fp16 of B column (l % 32); both halves of the wave
-// (l / 32) supply different K slots.  The sum over K does not care which K
-// index sits in which slot as long as A and B agree, so each lane takes 16
-// contiguous packed bytes (32 K elements) of its row per 64-K group: half 0
-// takes K [0, 32) and half 1 takes K [32, 64) of the group, one dword (8 K)
-// per instruction.  Every dword lies inside one 16-element scale block.
-//
-// Accumulator layout of v_mfma_f32_32x32x16_f16: lane l, register r holds
-// row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
-#include "launch.h"
+// kernels.hip -- gfx950 (CDNA4) NVFP4 GEMM kernels staged through registers:
+// the one- and four-wave 128 x 128 tiles for K % 128 != 0 or byte-path
+// scales, the small-M stream and panel kernels with their in-kernel K-split
+// sum, and the scale-layout conversion; the grouped launcher.  The
+// direct-to-LDS 128 x 128 kernels are in kernels_dma.hip; the scale mapping
+// and MFMA operand placement all kernels share are described in
+// kernel_common.h.
+#include "kernel_common.h"
 
 namespace nvfp4 {
 namespace {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// Raw (unstrided) buffer resource: loads at offsets >= num_records return 0.
-constexpr int kBufferWord3 = 0x00020000;
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes)
-{
-    int n = bytes >= 0x7fffffffull ? 0x7fffffff : (int)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kBufferWord3);
-}
-
-// 8 packed e2m1 codes -> 8 fp16 values times the broadcast scale s.
-__device__ inline half8_t decode8(uint32_t packed, half2_t s)
-{
-    half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 0);
-    half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 1);
-    half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2);
-    half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 3);
-    h0 *= s;
-    h1 *= s;
-    h2 *= s;
-    h3 *= s;
-    return (half8_t){h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
-
-__device__ inline half2_t bcast_lo(half2_t v) { return (half2_t){v.x, v.x}; }
-__device__ inline half2_t bcast_hi(half2_t v) { return (half2_t){v.y, v.y}; }
-
-// A problem table read from device memory (device-resident grouped calls).
-struct DevTableView {
-    int num_groups;
-    const int *prefix;
-    const GemmDesc *g;
-};
-
-// Workgroup -> (group, tile) through the exclusive prefix over tile counts
-// (the last group whose prefix entry is <= w: empty groups are passed over).
-template <class Table>
-__device__ inline int find_group(const Table &t, int w)
-{
-    int lo = 0, hi = t.num_groups;
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (t.prefix[mid] <= w)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    return lo;
-}
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: one workgroup of a single wave per 128 x 128 output tile.
@@ -108,22 +29,6 @@ __device__ inline int find_group(const Table &t, int w)
 // row-wise writes and the MFMA-layout reads bank-conflict free, and keeps two
 // stages at 36 KiB so that four workgroups fit a CU's 160 KiB.
 // ---------------------------------------------------------------------------
-namespace tiled {
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int kRowBytes = BK / 2;          // 64 packed bytes per row per K tile
-constexpr int kStride = kRowBytes;         // swizzled, unpadded LDS row
-constexpr int kSfBytes = BK / 16;          // 8 scale bytes per row per K tile
-constexpr int kAOff = 0;
-constexpr int kBOff = BM * kStride;
-constexpr int kSaOff = kBOff + BN * kStride;
-constexpr int kSbOff = kSaOff + BM * kSfBytes;
-constexpr int kStageBytes = kSbOff + BN * kSfBytes; // 18432
-// byte offset of 16-byte chunk c of row r within an A or B stage
-__device__ inline int swz(int r, int c) { return r * kStride + ((c ^ ((r >> 2) & 3)) << 4); }
-constexpr int kCStride = BN * 2 + 16;      // bytes per fp16 C row in LDS
-static_assert(2 * kStageBytes >= BM * kCStride, "C tile reuses the stages");
-} // namespace tiled
-
 struct TiledSlot {
     u32x4 a[8];   // A chunk c = 64 j + lane: row c / 4, bytes 16 (c % 4)
     u32x4 b[8];
@@ -137,11 +42,6 @@ struct TiledSlot {
 // tiles four ways (one per SIMD of the CU, each with its own LDS stages) and
 // their sums are added through LDS at the end: used when tiles alone would
 // leave SIMDs idle.
-// Cache policy of the partial-tile exchange: sc1, the bit agent-scope atomic
-// accesses carry, so the stores and loads are coherent across the XCD L2s
-// without a whole-cache write-back or invalidate.
-constexpr int kCoherent = 16;
-
 // kWaves = 1: one wave owns a 128 x 128 tile.  kWaves = 4: four waves split
 // each tile's K and add their sums through LDS.
 template <bool kVec, int kWaves>
@@ -923,523 +823,6 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 }
 
 // ----------------------------------------------------------------------------
-// One-wave 128 x 128 tile kernel with direct global -> LDS loads (gfx950
-// buffer_load ... lds, 16 bytes per lane for A and B, 4 for the scales): no
-// register staging slot, so the registers it would hold go to the compute.
-// Two LDS stages in one array: tile kt + 1 streams into one while tile kt is
-// computed from the other, with explicit waits (below).  The 16-byte chunk
-// swizzle of the register-staged kernel is kept by choosing each lane's
-// global chunk: a load instruction fills 16 rows of 64 bytes, lane i landing
-// at row i / 4, physical chunk i % 4, so it fetches logical chunk (i % 4) ^
-// ((row / 4) % 4).  Vector path only (K % 128 == 0, 8-byte aligned scales).
-//
-// kPow2: every scale is a power of two, E4M3 codes with a zero mantissa and
-// exponent field e in 1..15 (2^-6 .. 2^8).  Then a s_a b s_b = (a b) 2^(ea +
-// eb), so the packed codes go to the scaled FP4 MFMA (v_mfma_scale_f32_
-// 32x32x64_f8f6f4) undecoded, with the scales as E8M0 exponents (e + 120).
-// That MFMA applies one scale per lane to 32 K slots; NVFP4 scales cover 16,
-// so each lane's 32 slots hold one 16-value block and 16 zeros: a step of
-// four lanes-halves covers blocks 2 s (lanes 0-31) and 2 s + 1 (lanes 32-63)
-// of every row, 32 real K per 32x32 MFMA (the fp16 path needs two MFMAs and
-// eight decode instructions per fragment for the same 32 K).  Other scale
-// codes are outside this path's contract (their mantissa bits are ignored).
-//
-// kScales, how the scales reach LDS.  kScalesPlain: [rows][K/16] scales, four
-// 4-byte loads per lane per operand and K tile (8 bytes from each of 32 rows
-// per instruction).  kScalesPairs (every K % 256 == 0): [rows][K/16] scales of
-// two K tiles at once, one 16-byte load per lane and 64 rows (a row's 8 + 8
-// bytes are adjacent), into one of two pair buffers (rows of 16 bytes; tile
-// kt's 8 bytes at 8 (kt % 2)), half the instructions and half the cache lines
-// per K tile.  The pair buffers reuse the stages' scale areas plus 4 KiB.
-// kScalesBlocked: SFA and SFB arrive in the blocked layout the pages' kernels
-// consume (512-byte atoms of 128 rows x 4 scale blocks, atoms of a 128-row
-// tile in K order; row r, block c of an atom at (r % 32) * 16 + (r / 32) * 4 +
-// c).  A 128 x 128 tile's scales for one 128-K tile are then its two
-// consecutive atoms, 1 KiB, one 16-byte direct load per lane per operand,
-// kept in LDS as they are; the compute reads row 32 i + l32's four blocks of
-// 64-K group g at 512 g + 16 l32 + 4 i.  Rows past M or N are the layout's
-// zero padding.
-typedef __attribute__((address_space(3))) void lds_void;
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-constexpr int kScalesPlain = 0, kScalesPairs = 1, kScalesBlocked = 2;
-
-// The 16 MFMAs of one power-of-two step: the scale bytes sit in byte kSel of
-// each lane's exponent dwords.
-template <int kSel>
-__device__ inline void mfma_pow2_step(f32x16 (&acc)[4][4], const i32x8 (&fa)[4], const i32x8 (&fb)[4],
-                                      const uint32_t (&ea)[4], const uint32_t (&eb)[4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4, kSel,
-                                                                         (int)ea[i], kSel, (int)eb[j]);
-}
-
-// The work of one workgroup (one 128 x 128 tile); Table is the by-value
-// GroupTable of an ordinary launch or a DevTableView of a device-resident one.
-//
-// kWaves = 4: four waves share the tile, each running the pipeline above over
-// a quarter of its K tiles (whole pairs of K tiles with paired scales) in an
-// LDS region of its own (the four regions fill the CU's 160 KiB), with no
-// barrier in the K loop.  Their partial tiles are then added through LDS in a
-// fixed order, (w0 + w2) + (w1 + w3), and wave 0 writes C.  One workgroup per
-// CU: used where tiles are too few for one wave per tile to fill the SIMDs.
-template <bool kPow2, int kScales, int kWaves, class Table>
-__device__ inline void tiled_dma_tile(const Table &tab, const int w)
-{
-    constexpr bool kBlocked = kScales == kScalesBlocked;
-    constexpr bool kPairs = kScales == kScalesPairs;
-    static_assert(!kPow2 || kScales == kScalesPlain, "the power-of-two path reads plain scales");
-    static_assert(kWaves == 1 || (!kPow2 && !kBlocked), "four-wave tiles read plain scales");
-    using namespace tiled;
-    constexpr int kWaveLds = 2 * kStageBytes + (kPairs ? 4096 : 0);
-    static_assert(kWaves * kWaveLds <= 160 * 1024, "the wave regions fit in LDS");
-    __shared__ __attribute__((aligned(16))) uint8_t stages_all[kWaves * kWaveLds];
-    const int wv = kWaves > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
-    uint8_t *const stages = kWaves == 1 ? stages_all : stages_all + wv * kWaveLds;
-    uint8_t *const stage0 = stages;
-    uint8_t *const stage1 = stages + kStageBytes;
-    // pair buffers (kPairs): A's in the stages' 2 KiB scale areas, B's past them
-    auto qa = [&](int q) { return stages + q * kStageBytes + kSaOff; };
-    auto qb = [&](int q) { return stages + 2 * kStageBytes + 2048 * q; };
-
-    const int gi = find_group(tab, w);
-    const GemmDesc &d = tab.g[gi];
-    const int r = w - tab.prefix[gi];
-    const int tm = r % d.tiles_m;
-    const int tn = r / d.tiles_m;
-    const int M = d.M, N = d.N, K = d.K;
-    const int row0 = tm * BM, col0 = tn * BN;
-    const int lane = threadIdx.x & 63;
-    const int h = lane >> 5;
-    const int l32 = lane & 31;
-    const uint32_t sh = h * 16;
-
-    const int kb_row = K / 2;
-    const int ks_row = K / 16;
-    const int nkt = K / BK;
-    // this wave's K tiles [kt_lo, kt_hi): all of them, or a quarter (whole
-    // pairs of K tiles when the scales move in pairs)
-    const int kt_lo = kWaves == 1 ? 0 : kPairs ? 2 * ((nkt / 2) * wv / kWaves) : nkt * wv / kWaves;
-    const int kt_hi = kWaves == 1 ? nkt : kPairs ? 2 * ((nkt / 2) * (wv + 1) / kWaves) : nkt * (wv + 1) / kWaves;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
-    // blocked scales: one 128-row tile's atoms, K / 64 of them (K % 128 == 0)
-    const long atoms_bytes = (long)(K / 64) * 512;
-    const __amdgpu_buffer_rsrc_t rSA =
-        kBlocked ? make_rsrc(d.SFA + (long)tm * atoms_bytes, (uint64_t)atoms_bytes)
-                 : make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
-    const __amdgpu_buffer_rsrc_t rSB =
-        kBlocked ? make_rsrc(d.SFB + (long)tn * atoms_bytes, (uint64_t)atoms_bytes)
-                 : make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
-
-    // data: instruction j covers rows 16 j .. 16 j + 15
-    const int drow = lane >> 2;
-    const uint32_t d_off = (uint32_t)(drow * kb_row + (((lane & 3) ^ ((drow >> 2) & 3)) << 4));
-    // scales: instruction j covers rows 32 j .. 32 j + 31 (two dwords each)
-    const uint32_t s_off = (uint32_t)((lane >> 1) * ks_row + (lane & 1) * 4);
-
-    // tile kt into stage `st` (tiles past kt_hi read as zero)
-    auto issue = [&](uint8_t *st, int kt) {
-        const bool live = kt < kt_hi;
-        const uint32_t kb = (uint32_t)kt * kRowBytes, ks = (uint32_t)kt * kSfBytes;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t off = live ? d_off + (uint32_t)(16 * j * kb_row) + kb : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(st + kAOff + 1024 * j), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(st + kBOff + 1024 * j), 16, off, 0, 0, 0);
-        }
-        if (kPairs) {
-            // scales move in pairs of K tiles (issue_pair)
-        } else if (kBlocked) {
-            // the tile's two atoms of this K tile: 1 KiB per operand
-            const uint32_t off = live ? (uint32_t)kt * 1024 + (uint32_t)(lane * 16) : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff), 16, off, 0, 0, 0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t off = live ? s_off + (uint32_t)(32 * j * ks_row) + ks : kOutOfRange;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(st + kSaOff + 256 * j), 4, off, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(st + kSbOff + 256 * j), 4, off, 0, 0, 0);
-            }
-        }
-    };
-    // scales of K tiles kt and kt + 1 (kt even) into pair buffer q: instruction
-    // j covers rows 64 j .. 64 j + 63, lane i row 64 j + i
-    auto issue_pair = [&](int q, int kt) {
-        const bool live = kt < kt_hi;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t off = live ? (uint32_t)((64 * j + lane) * ks_row + kt * kSfBytes) : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_void *)(qa(q) + 1024 * j), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_void *)(qb(q) + 1024 * j), 16, off, 0, 0, 0);
-        }
-    };
-
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = (f32x16){};
-
-    // MFMA work of the 128-K tile in stage st: two 64-K groups g.  Issue
-    // order (scheduling groups): the LDS reads, the scale conversion and
-    // first decode step, then every MFMA followed by the next step's decode
-    // VALU (4 per MFMA, 5 across the group boundary, where the second
-    // group's scales and first step are decoded), then the last step's MFMAs.
-    // (kPairs: the scales come from pair buffer q, tile half `half`)
-    auto compute = [&](const uint8_t *st, int q, int half) {
-        half2_t ca[2][4], cb[2][4];
-        u32x4 pa[2][4], pb[2][4];
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if constexpr (kPairs) {
-                    const int o = (32 * i + l32) * 16 + 8 * half + 4 * g;
-                    const uint32_t wa = *(const uint32_t *)(qa(q) + o);
-                    const uint32_t wb = *(const uint32_t *)(qb(q) + o);
-                    ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa >> sh, 1.0f, false);
-                    cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb >> sh, 1.0f, false);
-                } else if constexpr (kBlocked) {
-                    // blocks 4 g .. 4 g + 3 of row 32 i + l32: word i of the row's 16 bytes in atom g
-                    const uint32_t wa = *(const uint32_t *)(st + kSaOff + 512 * g + 16 * l32 + 4 * i);
-                    const uint32_t wb = *(const uint32_t *)(st + kSbOff + 512 * g + 16 * l32 + 4 * i);
-                    ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa >> sh, 1.0f, false);
-                    cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb >> sh, 1.0f, false);
-                } else {
-                    const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
-                    const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
-                    ca[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? va.y : va.x) >> sh, 1.0f, false);
-                    cb[g][i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((g ? vb.y : vb.x) >> sh, 1.0f, false);
-                }
-                pa[g][i] = *(const u32x4 *)(st + kAOff + swz(32 * i + l32, 2 * g + h));
-                pb[g][i] = *(const u32x4 *)(st + kBOff + swz(32 * i + l32, 2 * g + h));
-            }
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                half8_t fa[4], fb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    fa[i] = decode8(pa[g][i][q], q < 2 ? bcast_lo(ca[g][i]) : bcast_hi(ca[g][i]));
-                    fb[i] = decode8(pb[g][i][q], q < 2 ? bcast_lo(cb[g][i]) : bcast_hi(cb[g][i]));
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            }
-        __builtin_amdgcn_sched_group_barrier(0x100, 32, 0); // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 80, 0); // group 0 scales + step 0 decode
-#pragma unroll
-        for (int k = 0; k < 48; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) { // group 1 scales + step 0 under group 0's last MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < 48; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    };
-
-    // power-of-two scales: step s (blocks 2 s + h of every row) of the 128-K
-    // tile in stage st on the scaled FP4 MFMA
-    auto compute_pow2 = [&](const uint8_t *st) {
-        // E8M0 exponents of the lane's rows: dword d holds blocks 4 d + h ..
-        // (shifted down by h bytes), so block 2 s + h sits in byte 2 (s % 2)
-        // of dword s / 2
-        uint32_t ea[2][4], eb[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x2 va = *(const u32x2 *)(st + kSaOff + (32 * i + l32) * kSfBytes);
-            const u32x2 vb = *(const u32x2 *)(st + kSbOff + (32 * i + l32) * kSfBytes);
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                ea[d][i] = ((va[d] >> (8 * h + 3)) & 0x0F0F0F0Fu) + 0x78787878u;
-                eb[d][i] = ((vb[d] >> (8 * h + 3)) & 0x0F0F0F0Fu) + 0x78787878u;
-            }
-        }
-#pragma unroll
-        for (int st4 = 0; st4 < 4; ++st4) {
-            i32x8 fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x2 xa = *(const u32x2 *)(st + kAOff + swz(32 * i + l32, st4) + 8 * h);
-                const u32x2 xb = *(const u32x2 *)(st + kBOff + swz(32 * i + l32, st4) + 8 * h);
-                fa[i] = (i32x8){(int)xa.x, (int)xa.y, 0, 0, 0, 0, 0, 0};
-                fb[i] = (i32x8){(int)xb.x, (int)xb.y, 0, 0, 0, 0, 0, 0};
-            }
-            if (st4 & 1)
-                mfma_pow2_step<2>(acc, fa, fb, ea[st4 >> 1], eb[st4 >> 1]);
-            else
-                mfma_pow2_step<0>(acc, fa, fb, ea[st4 >> 1], eb[st4 >> 1]);
-        }
-    };
-
-    // The compiler does not order these loads' LDS writes before the reads
-    // of the same array, so the waits are explicit: before a stage is read,
-    // at most the other stage's kIssued loads may still be in flight
-    // (s_waitcnt simm16 on gfx9: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
-    // lgkmcnt 11:8 left at their maxima).
-    constexpr int kIssued = 8 + 8 + (kPairs ? 4 : kBlocked ? 2 : 8);
-    constexpr int kWaitOther = ((kIssued >> 4) << 14) | (15 << 8) | (7 << 4) | (kIssued & 15);
-    if (kPairs && kt_hi > kt_lo) {
-        // stage data as below; scale pairs one iteration ahead.  Before each
-        // compute, this iteration's data (16) and next pair (4), or next data
-        // stage, may still be in flight: every wait leaves kIssued.
-        issue(stage0, kt_lo);
-        issue_pair(0, kt_lo);
-        for (int kt = kt_lo, q = 0; kt < kt_hi; kt += 2, q ^= 1) {
-            issue(stage1, kt + 1);
-            issue_pair(q ^ 1, kt + 2);
-            SCHED_FENCE();
-            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage0 and pair q have landed
-            SCHED_FENCE();
-            compute(stage0, q, 0);
-            SCHED_FENCE();
-            issue(stage0, kt + 2);
-            SCHED_FENCE();
-            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage1 has landed
-            SCHED_FENCE();
-            compute(stage1, q, 1);
-            SCHED_FENCE();
-        }
-    } else if (kt_hi > kt_lo) {
-        issue(stage0, kt_lo);
-        for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-            issue(stage1, kt + 1);
-            SCHED_FENCE();
-            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage0 has landed
-            SCHED_FENCE();
-            if (kPow2)
-                compute_pow2(stage0);
-            else
-                compute(stage0, 0, 0);
-            SCHED_FENCE();
-            issue(stage0, kt + 2);
-            SCHED_FENCE();
-            __builtin_amdgcn_s_waitcnt(kWaitOther); // stage1 has landed
-            SCHED_FENCE();
-            // with an odd tile count the last stage1 tile is out of range:
-            // zeros, adding exact zeros (no branch around the accumulators)
-            if (kPow2)
-                compute_pow2(stage1);
-            else
-                compute(stage1, 0, 0);
-            SCHED_FENCE();
-        }
-    }
-
-    if constexpr (kWaves > 1) {
-        // add the four partial tiles: 16-byte pieces (i, j, e / 4) of each
-        // lane, [piece][lane], in slots of 64 KiB over the whole LDS
-        __builtin_amdgcn_s_waitcnt(0); // this wave's trailing zero loads have landed
-        __syncthreads();               // every wave is past its K loop
-        float *red = (float *)stages_all;
-        auto put = [&](int slot) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        *(float4 *)(red + slot * 16384 + (((i * 4 + j) * 4 + e) * 64 + lane) * 4) =
-                            (float4){acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]};
-        };
-        auto add = [&](int slot) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float4 v = *(const float4 *)(red + slot * 16384 + (((i * 4 + j) * 4 + e) * 64 + lane) * 4);
-                        acc[i][j][4 * e] += v.x;
-                        acc[i][j][4 * e + 1] += v.y;
-                        acc[i][j][4 * e + 2] += v.z;
-                        acc[i][j][4 * e + 3] += v.w;
-                    }
-        };
-        if (wv >= 2)
-            put(wv - 2);
-        __syncthreads();
-        if (wv < 2)
-            add(wv);
-        __syncthreads();
-        if (wv == 1)
-            put(0);
-        __syncthreads();
-        if (wv != 0)
-            return;
-        add(0);
-    }
-
-    // epilogue: fp16 (round to nearest even) rows 0..63 into stage0 and rows
-    // 64..127 into stage1 (the loop's last reads are done: each wave reads
-    // only what it wrote), then 16-byte row-contiguous stores masked to M x N
-    // (the tile's trailing zero-tile loads were out of range: nothing lands)
-    __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = 32 * i + (e >> 2) * 8 + h * 4 + (e & 3);
-                const int col = 32 * j + l32;
-                uint8_t *sC = row < 64 ? stage0 : stage1;
-                *(uint16_t *)(sC + (row & 63) * kCStride + col * 2) = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e]);
-            }
-    const bool vec_ok = (N % 8 == 0) && ((((uintptr_t)d.C) & 15) == 0);
-#pragma unroll 4
-    for (int s2 = 0; s2 < BM * BN / 8 / 64; ++s2) {
-        const int seg = s2 * 64 + lane;
-        const int row = seg >> 4, c8 = (seg & 15) * 8;
-        const int grow = row0 + row, gcol = col0 + c8;
-        if (grow >= M)
-            continue;
-        const uint8_t *sC = row < 64 ? stage0 : stage1;
-        uint16_t *dst = d.C + (long)grow * N + gcol;
-        const uint16_t *src = (const uint16_t *)(sC + (row & 63) * kCStride + c8 * 2);
-        if (vec_ok && gcol + 8 <= N) {
-            *(u32x4 *)dst = *(const u32x4 *)src;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (gcol + e < N)
-                    dst[e] = src[e];
-        }
-    }
-}
-
-template <bool kPow2, int kScales>
-__global__ __launch_bounds__(64) void gemm_tiled_dma_kernel(GroupTable tab)
-{
-    tiled_dma_tile<kPow2, kScales, 1>(tab, (int)blockIdx.x);
-}
-
-// Four waves per 128 x 128 tile, each over a quarter of its K.
-template <int kScales>
-__global__ __launch_bounds__(256) void gemm_tiled_dma4_kernel(GroupTable tab)
-{
-    tiled_dma_tile<false, kScales, 4>(tab, (int)blockIdx.x);
-}
-
-// Device-resident grouped launch: the table the plan kernel left in the
-// workspace; workgroups past its tile total return at once.
-__global__ __launch_bounds__(64) void gemm_tiled_dma_dev_kernel(const uint8_t *ws)
-{
-    const DevHeader hd = *(const DevHeader *)ws;
-    if ((int)blockIdx.x >= hd.total_tiles)
-        return;
-    const DevTableView view = {hd.num_groups, (const int *)(ws + 16),
-                               (const GemmDesc *)(ws + dev_desc_offset(hd.num_groups))};
-    tiled_dma_tile<false, kScalesPlain, 1>(view, (int)blockIdx.x);
-}
-
-// Plan of a device-resident grouped call, one workgroup: each thread checks
-// up to four consecutive problems against the one-wave kernel's contract
-// (sizes >= 0, K % 128 == 0 and <= 2^24, pointers present, A and B 16-byte
-// and the scales 8-byte aligned, at most 2^24 tiles), writes their GemmDesc
-// and tile counts (zero when outside the contract or empty), and a
-// workgroup scan (64-bit, clamped to INT32_MAX) gives the exclusive prefix.
-constexpr int kPlanThreads = 1024;
-__global__ __launch_bounds__(kPlanThreads) void plan_device_table_kernel(const ProblemRecord *problems, int G,
-                                                                          uint8_t *ws)
-{
-    __shared__ long long part[kPlanThreads];
-    __shared__ int bad[kPlanThreads];
-    int *prefix = (int *)(ws + 16);
-    GemmDesc *desc = (GemmDesc *)(ws + dev_desc_offset(G));
-    const int t = threadIdx.x;
-    const int per = (G + kPlanThreads - 1) / kPlanThreads; // at most 4 (G <= 4096)
-    const int g0 = t * per;
-    long long local[4] = {0, 0, 0, 0};
-    long long sum = 0;
-    int nbad = 0;
-    for (int i = 0; i < per && i < 4; ++i) {
-        const int g = g0 + i;
-        if (g >= G)
-            break;
-        const ProblemRecord p = problems[g];
-        bool ok = p.M >= 0 && p.N >= 0 && p.K >= 0 && p.K % 128 == 0 && p.K <= (1 << 24);
-        const bool empty = p.M == 0 || p.N == 0;
-        long long tiles = 0;
-        if (ok && !empty) {
-            ok = p.C != nullptr &&
-                 (p.K == 0 || (p.A != nullptr && p.SFA != nullptr && p.B != nullptr && p.SFB != nullptr &&
-                               ((((uintptr_t)p.A) | ((uintptr_t)p.B)) & 15) == 0 &&
-                               ((((uintptr_t)p.SFA) | ((uintptr_t)p.SFB)) & 7) == 0));
-            tiles = (long long)((p.M + tiled::BM - 1) / tiled::BM) * ((p.N + tiled::BN - 1) / tiled::BN);
-            if (tiles > (1 << 24))
-                ok = false;
-        }
-        if (!ok) {
-            ++nbad;
-            tiles = 0;
-        }
-        GemmDesc d;
-        d.A = p.A;
-        d.SFA = p.SFA;
-        d.B = p.B;
-        d.SFB = p.SFB;
-        d.C = p.C;
-        d.M = p.M;
-        d.N = p.N;
-        d.K = p.K;
-        d.tiles_m = p.M > 0 ? (p.M + tiled::BM - 1) / tiled::BM : 1;
-        desc[g] = d;
-        local[i] = tiles;
-        sum += tiles;
-    }
-    part[t] = sum;
-    bad[t] = nbad;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const long long v = t >= off ? part[t - off] : 0;
-        const int b = t >= off ? bad[t - off] : 0;
-        __syncthreads();
-        part[t] += v;
-        bad[t] += b;
-        __syncthreads();
-    }
-    long long run = part[t] - sum;
-    for (int i = 0; i < per && i < 4; ++i) {
-        const int g = g0 + i;
-        if (g >= G)
-            break;
-        prefix[g] = (int)(run < 0x7fffffffLL ? run : 0x7fffffffLL);
-        run += local[i];
-    }
-    if (t == kPlanThreads - 1) {
-        const long long total = part[t];
-        const int tot = (int)(total < 0x7fffffffLL ? total : 0x7fffffffLL);
-        prefix[G] = tot;
-        DevHeader h;
-        h.num_groups = G;
-        h.total_tiles = tot;
-        h.invalid_groups = bad[t];
-        h.reserved = 0;
-        *(DevHeader *)ws = h;
-    }
-}
-
-// ----------------------------------------------------------------------------
 // Scale layout conversion (see ScaleConvTable).  A workgroup of 256 threads
 // takes one 128-row tile and kConvAtoms consecutive atoms (4 KiB): the blocked
 // side moves as coalesced 16-byte lane pieces, the plain side through LDS as
@@ -1559,66 +942,14 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % tiled::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 7) == 0;
+        if (cfg == kTile128x128Blocked || cfg == kTile128x128Pow2 || vec)
+            return launch_tiled_dma(table, cfg, stream);
+        // K % 128 != 0 or byte-path scales: the K tile goes through registers
         const bool four = cfg == kTile128x128K4;
-        if (cfg == kTile128x128Blocked) {
-            // blocked scales move in 16-byte pieces: 16-byte aligned arrays
-            bool ok = true;
-            for (int g = 0; g < table.num_groups; ++g)
-                ok = ok && (table.g[g].K % tiled::BK) == 0 &&
-                     ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
-            if (!ok)
-                return hipErrorInvalidValue;
-            void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<false, kScalesBlocked>, dim3(tiles), dim3(64), dargs, 0, stream);
-        }
-        if (cfg == kTile128x128Pow2) {
-            if (!vec)
-                return hipErrorInvalidValue;
-            void *dargs[] = {const_cast<GroupTable *>(&table)};
-            return hipLaunchKernel((const void *)gemm_tiled_dma_kernel<true, kScalesPlain>, dim3(tiles), dim3(64), dargs, 0, stream);
-        }
-        if (!four && vec) {
-            bool pairs = true; // even K tile counts: scales in pairs of K tiles
-            for (int g = 0; g < table.num_groups; ++g)
-                pairs = pairs && (table.g[g].K % (2 * tiled::BK)) == 0;
-            void *dargs[] = {const_cast<GroupTable *>(&table)};
-            const void *fn = pairs ? (const void *)gemm_tiled_dma_kernel<false, kScalesPairs>
-                                   : (const void *)gemm_tiled_dma_kernel<false, kScalesPlain>;
-            return hipLaunchKernel(fn, dim3(tiles), dim3(64), dargs, 0, stream);
-        }
-        if (four && vec) {
-            bool pairs = true; // even K tile counts: scales in pairs of K tiles
-            for (int g = 0; g < table.num_groups; ++g)
-                pairs = pairs && (table.g[g].K % (2 * tiled::BK)) == 0;
-            void *dargs[] = {const_cast<GroupTable *>(&table)};
-            const void *fn = pairs ? (const void *)gemm_tiled_dma4_kernel<kScalesPairs>
-                                   : (const void *)gemm_tiled_dma4_kernel<kScalesPlain>;
-            return hipLaunchKernel(fn, dim3(tiles), dim3(256), dargs, 0, stream);
-        }
-        const void *fn = four ? (vec ? (const void *)gemm_tiled_kernel<true, 4> : (const void *)gemm_tiled_kernel<false, 4>)
-                              : (vec ? (const void *)gemm_tiled_kernel<true, 1> : (const void *)gemm_tiled_kernel<false, 1>);
+        const void *fn = four ? (const void *)gemm_tiled_kernel<false, 4> : (const void *)gemm_tiled_kernel<false, 1>;
         return hipLaunchKernel(fn, dim3(tiles), dim3(four ? 256 : 64), args, 0, stream);
     }
     }
-}
-
-hipError_t launch_device_table(const ProblemRecord *problems, int num_groups, int max_tiles, void *workspace,
-                               hipStream_t stream)
-{
-    if (num_groups <= 0 || max_tiles <= 0)
-        return hipSuccess;
-    if (num_groups > 4 * kPlanThreads)
-        return hipErrorInvalidValue;
-    uint8_t *ws = (uint8_t *)workspace;
-    void *pargs[] = {const_cast<ProblemRecord **>(&problems), &num_groups, &ws};
-    hipError_t e = hipLaunchKernel((const void *)plan_device_table_kernel, dim3(1), dim3(kPlanThreads), pargs, 0,
-                                   stream);
-    if (e != hipSuccess)
-        return e;
-    const uint8_t *cws = ws;
-    void *gargs[] = {&cws};
-    return hipLaunchKernel((const void *)gemm_tiled_dma_dev_kernel, dim3((unsigned)max_tiles), dim3(64), gargs, 0,
-                           stream);
 }
 
 hipError_t launch_scale_conversion(const ScaleConvTable &table, hipStream_t stream)

@@ -115,6 +115,17 @@ inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_
 
 // Launches one grouped pass (table already filled, prefix included).
 hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, hipStream_t stream);
+// The direct-to-LDS 128 x 128 kernels (kernels_dma.hip): one wave per tile
+// (kTile128x128, kTile128x128Pow2, kTile128x128Blocked) or four
+// (kTile128x128K4).  Every K % 128 == 0 and the scales 8-byte aligned
+// (16-byte for blocked scales), else hipErrorInvalidValue.
+hipError_t launch_tiled_dma(const GroupTable &table, TileConfig cfg, hipStream_t stream);
+// Its parts, one source each (checked arguments, at least one tile): plain
+// scales one wave per tile, gathered or in pairs of K tiles; blocked or
+// power-of-two scales; four waves per tile.
+hipError_t launch_dma_one_wave(const GroupTable &table, bool pairs, hipStream_t stream);
+hipError_t launch_dma_special(const GroupTable &table, TileConfig cfg, hipStream_t stream);
+hipError_t launch_dma_four_wave(const GroupTable &table, bool pairs, hipStream_t stream);
 
 // Scale-layout conversion, batched: entry e moves the scales of a
 // rows[e] x (kb[e] = K/16) matrix between the plain [rows][K/16] layout and

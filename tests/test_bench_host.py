@@ -1,5 +1,4 @@
 """Host-side logic of bench.py, on the CPU (no GPU call)."""
-import hashlib
 import os
 import subprocess
 import sys
@@ -22,8 +21,7 @@ def test_refuses_more_than_one_gpu():
 
 
 def test_traffic_only_for_the_current_kernel_source(tmp_path, monkeypatch):
-    with open(bench.KERNEL_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = bench.kernel_source_sha()
     table = tmp_path / "traffic.txt"
     table.write_text("# comment\nwl_a %s 123\nwl_b %s 456\n" % (sha, "0" * 64))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(table))
