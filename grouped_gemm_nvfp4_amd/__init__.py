@@ -4,6 +4,7 @@ The computation lives in ``libnvfp4.so`` (hand-written HIP for gfx950 behind
 the C ABI of include/nvfp4.h); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
+    NVFP4_MAX_GROUPS,
     Nvfp4Error,
     abi_version,
     gemm_plan,

@@ -17,6 +17,7 @@ NVFP4_OK = 0
 NVFP4_ERROR_INVALID_VALUE = 1
 NVFP4_ERROR_NOT_SUPPORTED = 2
 NVFP4_ERROR_LAUNCH = 3
+NVFP4_MAX_GROUPS = 4096  # groups per grouped call
 
 EXPORTED = [
     "nvfp4_gemm", "nvfp4_group_gemm", "nvfp4_gemm_plan", "nvfp4_group_gemm_plan",

@@ -36,6 +36,16 @@ def test_abi_version():
     assert g.abi_version() == 1
 
 
+def test_binding_constants_match_header():
+    text = open(HEADER).read()
+    defines = dict(re.findall(r"#define (NVFP4_[A-Z_]+) (-?\d+)", text))
+    assert int(defines["NVFP4_MAX_GROUPS"]) == g.NVFP4_MAX_GROUPS
+    assert int(defines["NVFP4_ABI_VERSION"]) == g.abi_version()
+    for name in ("NVFP4_OK", "NVFP4_ERROR_INVALID_VALUE", "NVFP4_ERROR_NOT_SUPPORTED", "NVFP4_ERROR_LAUNCH"):
+        m = re.search(name + r"\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(b, name), name
+
+
 def test_status_strings():
     for s in range(4):
         assert g.status_string(s).startswith("NVFP4_")

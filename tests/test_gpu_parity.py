@@ -403,6 +403,51 @@ def test_group_many_groups_multiple_launches(lib):
         assert_parity(got, c16, bound, "many-group %d" % i)
 
 
+@pytest.mark.parametrize("route", ["64-row", "128x128"])
+def test_group_at_max_groups(lib, route):
+    """NVFP4_MAX_GROUPS groups in one call (64 launches), ragged and empty
+    groups included, on each side of the planner's M threshold; compared in
+    full."""
+    rng = np.random.default_rng(41 if route == "64-row" else 45)
+    if route == "64-row":
+        shapes = [(int(rng.integers(1, 65)), int(rng.integers(1, 100)), 32 * int(rng.integers(0, 13)))
+                  for _ in range(lib.NVFP4_MAX_GROUPS)]
+        shapes[5], shapes[77] = (0, 64, 256), (17, 0, 64)
+    else:
+        shapes = [(int(rng.integers(1, 200)), int(rng.integers(1, 200)), 128 * int(rng.integers(1, 4)))
+                  for _ in range(lib.NVFP4_MAX_GROUPS)]
+        shapes[3], shapes[9] = (200, 130, 256), (0, 64, 128)
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["tile_m"] == (64 if route == "64-row" else 128) and info["split_k"] == 1
+    probs = inputs.draw_problems(42, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "max-groups %s group %d" % (route, i))
+
+
+@pytest.mark.parametrize("kernel_tile_n,max_n", [(64, 65), (32, 33)])
+def test_group_split_k_across_launches(lib, kernel_tile_n, max_n):
+    """A K-split plan over more groups than one launch takes: the launches of
+    one call share the tile counters and partial tiles, one after the other
+    (the 64 x 64 panel and the 64 x 32 stream kernels)."""
+    rng = np.random.default_rng(43)
+    count = 100 if kernel_tile_n == 64 else 90
+    shapes = [(int(rng.integers(1, 65)), int(rng.integers(max_n // 2 + 1, max_n)), 32 * int(rng.integers(128, 193)))
+              for _ in range(count)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["tile_n"] == kernel_tile_n and info["split_k"] > 1
+    probs = inputs.draw_problems(44, shapes)
+    for rep in range(2):  # the second call finds the counters the first left
+        outs = run_group(lib, probs)
+        for i, (p, got) in enumerate(zip(probs, outs)):
+            c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+            assert_parity(got, c16, bound, "split across launches tile_n %d call %d group %d"
+                          % (kernel_tile_n, rep, i))
+
+
 @pytest.mark.parametrize("index", [3, 4])
 def test_full_size_grouped_workloads(lib, index):
     probs = inputs.draw_workload(index)
