@@ -142,6 +142,29 @@ def test_all_ones_gives_K(K):
     assert np.all(C64 == 2 * K)
 
 
+def test_group_gemm_each_group_its_own_closed_form():
+    """Groups of different sizes, codes and scales: group g's product is its
+    own closed form (all ones -> K; scales 2 x 2 -> 4K; code 0xA = -1.0 on one
+    side -> -K), so a group computed with another group's sizes, buffers or
+    scales fails; an empty group gives an empty result."""
+    def ones(M, N, K, code_a=0x22, sa=0x38, sb=0x38):
+        return {"A": np.full((M, K // 2), code_a, dtype=np.uint8),
+                "SFA": np.full((M, K // 16), sa, dtype=np.uint8),
+                "B": np.full((N, K // 2), 0x22, dtype=np.uint8),
+                "SFB": np.full((N, K // 16), sb, dtype=np.uint8), "M": M, "N": N, "K": K}
+    groups = [ones(3, 5, 256), ones(0, 4, 64), ones(2, 7, 1024, sa=0x40, sb=0x40),
+              ones(6, 1, 96, code_a=0xAA)]
+    expected = [256.0, None, 4 * 1024.0, -96.0]
+    out = oracle.group_gemm(groups)
+    assert len(out) == len(groups)
+    for g, (C16, C64, bound), want in zip(groups, out, expected):
+        assert C64.shape == (g["M"], g["N"])
+        if want is None:
+            continue
+        assert np.all(C64 == want) and np.all(bound == abs(want))
+        assert np.all(C16.view(np.float16).astype(np.float64) == want)
+
+
 def test_overflow_rounds_to_infinity():
     K = 32
     A = np.full((2, K // 2), 0x77, dtype=np.uint8)  # 6.0
