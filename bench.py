@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1,
                     help="index into grouped_gemm_nvfp4_amd.inputs.WORKLOADS")
+    ap.add_argument("--shape", default=None, metavar="M,N,K",
+                    help="time one GEMM of these sizes (seeded inputs, seed %d) instead of a "
+                         "named workload" % SHAPE_SEED)
     ap.add_argument("--copies", type=int, default=0,
                     help="operand copies to cycle over (0: enough to exceed the caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -80,6 +83,20 @@ def parse():
 
 KERNEL_DIR = os.path.join(ROOT, "grouped_gemm_nvfp4_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+SHAPE_SEED = 2000  # inputs of a --shape run
+
+
+def parse_shape(text):
+    """'M,N,K' -> (M, N, K): positive sizes, K a multiple of 32."""
+    try:
+        M, N, K = (int(x) for x in text.split(","))
+    except ValueError:
+        raise SystemExit("--shape takes M,N,K (three integers), got %r" % text)
+    if min(M, N, K) < 1 or K % 32 != 0:
+        raise SystemExit("--shape needs M, N, K >= 1 and K a multiple of 32, got %r" % text)
+    return M, N, K
 
 
 def kernel_source_sha():
@@ -193,12 +210,20 @@ def main():
     from grouped_gemm_nvfp4_amd import _binding as b
 
     lib = g.load()
-    wl = inputs.WORKLOADS[args.workload]
     pow2 = args.scales == "pow2"
     if pow2 and args.scale_layout != "plain":
         print("--scales pow2 takes plain-layout scales only", file=sys.stderr)
         sys.exit(2)
-    probs = inputs.draw_workload(args.workload, inputs.POW2_SCALE_CODES if pow2 else inputs.SCALE_CODES)
+    codes = inputs.POW2_SCALE_CODES if pow2 else inputs.SCALE_CODES
+    if args.shape:
+        M, N, K = parse_shape(args.shape)
+        wl = inputs.Workload("gemm_%dx%dx%d" % (M, N, K), False, "single GEMM M=%d N=%d K=%d" % (M, N, K))
+        seed = SHAPE_SEED
+        probs = inputs.draw_problems(seed, [(M, N, K)], codes)
+    else:
+        wl = inputs.WORKLOADS[args.workload]
+        seed = inputs.workload_shapes(args.workload)[0]
+        probs = inputs.draw_workload(args.workload, codes)
     shapes = [(p.M, p.N, p.K) for p in probs]
     flops = inputs.flops(shapes)
     alg_bytes = inputs.algorithmic_bytes(shapes)
@@ -357,7 +382,7 @@ def main():
         "dtype": "e2m1" if pow2 else "f16",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
-                   "shapes_MNK": shapes, "seed": 1000 + args.workload,
+                   "shapes_MNK": shapes, "seed": seed,
                    "operand_copies": copies, "scale_layout": args.scale_layout,
                    "scales": args.scales, "table": args.table},
         "roofline": roof,

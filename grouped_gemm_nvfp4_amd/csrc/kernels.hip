@@ -590,13 +590,19 @@ struct PanelSlot {
 // each K tile are single-byte loads (lane l: row l), each masked against the
 // row's K / 16 blocks.
 //
+// kMB: 32-row MFMA blocks of A that hold rows.  With kMB == 1 (every group
+// of the launch has M <= 32, so rows 32..63 of the tile are past M) a wave
+// loads, stores and decodes only rows 0..31 of A and issues two MFMAs per
+// step instead of four; the other accumulators stay zero.
+//
 // With split_k > 1 every workgroup of a tile stores its partial tile, then
 // takes a ticket from the tile's counter; the last to arrive adds all
 // partial tiles in slice order (so the result does not depend on arrival
 // order), writes C and resets the counter to zero for the next launch.
-template <bool kVec>
+template <bool kVec, int kMB>
 __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable tab, float *partials, int *counters)
 {
+    static_assert(kMB == 1 || kMB == 2, "one or two 32-row blocks");
     using namespace panel;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kWaveBytes];
     __shared__ int s_last;
@@ -643,7 +649,8 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t off = cin ? line_off + (uint32_t)(8 * j * kb_row + kb) : kOutOfRange;
-            s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+            if (j < 4 * kMB)
+                s.a[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
             s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
         }
     };
@@ -655,7 +662,8 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off = live ? group_off + (uint32_t)(16 * i * ks_row + kt * kSfBytes) : kOutOfRange;
-            gsa[i] = __builtin_amdgcn_raw_buffer_load_b128(rSA, off, 0, 0);
+            if (i < 2 * kMB)
+                gsa[i] = __builtin_amdgcn_raw_buffer_load_b128(rSA, off, 0, 0);
             gsb[i] = __builtin_amdgcn_raw_buffer_load_b128(rSB, off, 0, 0);
         }
     };
@@ -682,14 +690,16 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
     auto put = [&](const PanelSlot &s, int u) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            *(u32x4 *)(wl + kAOff + swz(8 * j + lrow, c16)) = s.a[j];
+            if (j < 4 * kMB)
+                *(u32x4 *)(wl + kAOff + swz(8 * j + lrow, c16)) = s.a[j];
             *(u32x4 *)(wl + kBOff + swz(8 * j + lrow, c16)) = s.b[j];
         }
         if (kVec) {
             if (gtile == u) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    *(u32x4 *)(wl + kSfaOff + (16 * i + grow) * kSfBytes) = gsa[i];
+                    if (i < 2 * kMB)
+                        *(u32x4 *)(wl + kSfaOff + (16 * i + grow) * kSfBytes) = gsa[i];
                     *(u32x4 *)(wl + kSfbOff + (16 * i + grow) * kSfBytes) = gsb[i];
                 }
             }
@@ -711,7 +721,8 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
         u32x4 sa[2], sb[2]; // the 16 scale bytes of rows 32 o + l32
 #pragma unroll
         for (int o = 0; o < 2; ++o) {
-            sa[o] = *(const u32x4 *)(wl + kSfaOff + (32 * o + l32) * kSfBytes);
+            if (o < kMB)
+                sa[o] = *(const u32x4 *)(wl + kSfaOff + (32 * o + l32) * kSfBytes);
             sb[o] = *(const u32x4 *)(wl + kSfbOff + (32 * o + l32) * kSfBytes);
         }
 #pragma unroll
@@ -720,9 +731,11 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
             half2_t ca[2], cb[2]; // blocks 4i + 2h (.x) and 4i + 2h + 1 (.y)
 #pragma unroll
             for (int o = 0; o < 2; ++o) {
-                pa[o] = *(const u32x4 *)(wl + kAOff + swz(32 * o + l32, 2 * i + h));
+                if (o < kMB)
+                    pa[o] = *(const u32x4 *)(wl + kAOff + swz(32 * o + l32, 2 * i + h));
                 pb[o] = *(const u32x4 *)(wl + kBOff + swz(32 * o + l32, 2 * i + h));
-                ca[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[o][i] >> sh, 1.0f, false);
+                if (o < kMB)
+                    ca[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa[o][i] >> sh, 1.0f, false);
                 cb[o] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[o][i] >> sh, 1.0f, false);
             }
 #pragma unroll
@@ -730,11 +743,12 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
                 half8_t fa[2], fb[2];
 #pragma unroll
                 for (int o = 0; o < 2; ++o) {
-                    fa[o] = decode8(pa[o][q], q < 2 ? bcast_lo(ca[o]) : bcast_hi(ca[o]));
+                    if (o < kMB)
+                        fa[o] = decode8(pa[o][q], q < 2 ? bcast_lo(ca[o]) : bcast_hi(ca[o]));
                     fb[o] = decode8(pb[o][q], q < 2 ? bcast_lo(cb[o]) : bcast_hi(cb[o]));
                 }
 #pragma unroll
-                for (int oa = 0; oa < 2; ++oa)
+                for (int oa = 0; oa < kMB; ++oa)
 #pragma unroll
                     for (int ob = 0; ob < 2; ++ob)
                         acc[oa][ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[oa], fb[ob], acc[oa][ob], 0, 0, 0);
@@ -930,7 +944,12 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % panel::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
-        const void *fn = vec ? (const void *)gemm_panel_kernel<true> : (const void *)gemm_panel_kernel<false>;
+        // rows 32..63 of every tile past M: the one-block form
+        bool half = true;
+        for (int g = 0; g < table.num_groups; ++g)
+            half = half && table.g[g].M <= 32;
+        const void *fn = half ? (vec ? (const void *)gemm_panel_kernel<true, 1> : (const void *)gemm_panel_kernel<false, 1>)
+                              : (vec ? (const void *)gemm_panel_kernel<true, 2> : (const void *)gemm_panel_kernel<false, 2>);
         return hipLaunchKernel(fn, dim3(total), dim3(panel::kThreads), args, 0, stream);
     }
     case kTile128x128K4:

@@ -37,3 +37,10 @@ def test_cpu_baseline_reports_the_oracle():
     assert cpu["value"] > 0 and cpu["cores"] >= 1
     assert "workload" in cpu["sample"] or "rows" in cpu["sample"]
     assert "cpu_model" in cpu and "omp_num_threads" in cpu
+
+
+def test_shape_option_parsing():
+    assert bench.parse_shape("64,4096,7168") == (64, 4096, 7168)
+    for bad in ("64,4096", "64,4096,70", "0,8,32", "a,b,c"):
+        with pytest.raises(SystemExit):
+            bench.parse_shape(bad)

@@ -354,6 +354,34 @@ def test_group_small_m_split_k(lib):
         assert_parity(got, c16, bound, "small-M group %d" % i)
 
 
+@pytest.mark.parametrize("M,N,K,split", [
+    (1, 7168, 16384, 2),    # one row, scale groups of four K tiles
+    (32, 6144, 8192, 2),    # exactly one 32-row block
+    (17, 12288, 4128, 1),   # K % 256 != 0: byte scale loads, ragged last K tile
+    (32, 6400, 8224, 2),    # byte scale loads with a K split
+    (31, 7000, 8192, 2),    # ragged M and N
+])
+def test_panel_one_row_block(lib, M, N, K, split):
+    """M <= 32 on the panel kernel: only rows 0..31 of A are loaded and
+    decoded, two MFMAs per step."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["tile_n"] == 64 and info["split_k"] == split
+    p = inputs.draw_problems(5100 + M + K, [(M, N, K)])[0]
+    check_full(lib, p, "panel one block %dx%dx%d split %d" % (M, N, K, split))
+
+
+def test_group_panel_one_row_block(lib):
+    """A grouped panel launch whose groups all have M <= 32."""
+    shapes = [(32, 2048, 8192), (1, 2000, 8192), (20, 2048, 4096), (9, 1900, 8192)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["tile_n"] == 64 and info["split_k"] > 1
+    probs = inputs.draw_problems(39, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "panel one-block group %d" % i)
+
+
 def test_group_small_m_panel(lib):
     """Small-M groups whose 64 x 64 tiles fill the chip take the panel kernel
     with a K split; ragged N and M in some groups."""
