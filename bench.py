@@ -5,9 +5,11 @@
 
 One step is one call of the library (nvfp4_gemm for a single product,
 nvfp4_group_gemm for a grouped one) over one set of synthetic operands that
-already sit in device memory.  The default workload is the small-M,
-bandwidth-bound product M=64 N=7168 K=16384; ``--workload`` picks another of
-the named workloads in grouped_gemm_nvfp4_amd/inputs.py.
+already sit in device memory.  The headline workload is the large
+compute-bound product M = N = K = 8192; ``--workload`` picks another of the
+named workloads in grouped_gemm_nvfp4_amd/inputs.py and ``--shape M,N,K`` any
+single GEMM.  Unless ``--no-extras`` is given, every other named workload is
+timed in the same run, the same way, and reported under ``"workloads"``.
 
 Steps cycle over several identical copies of the operands whose total size
 exceeds the 256 MiB Infinity Cache plus the L2s, so each step reads its
@@ -17,9 +19,11 @@ Prints one JSON line: TFLOPS = sum 2*M*N*K / time, the roofline of the kernel
 (algorithmic bytes or flops per launch over its mean launch duration: the
 timed region measured with HIP events on the launch stream, divided by the
 number of steps), and the CPU oracle's throughput on a bounded sample of the
-same workload.  The roofline's "traffic" (HBM bytes per launch from the
+headline workload.  The roofline's "traffic" (HBM bytes per launch from the
 FETCH_SIZE and WRITE_SIZE counters) comes from profiles/hbm_traffic.txt and is
-reported only while the kernel sources it was measured on are unchanged.
+reported only while the kernel sources it was measured on are unchanged.  The
+GPU's graphics clock is sampled (amdsmi) while the headline workload runs
+back to back.
 
     python bench.py --copy-probe BYTES
 
@@ -33,6 +37,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -50,22 +55,31 @@ PEAK_FP4_TFLOPS = 10100.0
 CACHE_BYTES = 256 * 2 ** 20 + 8 * 4 * 2 ** 20  # Infinity Cache + 8 XCD L2s
 
 METRIC = "TFLOPS (2MNK/t) NVFP4 GEMM & grouped GEMM; % FP4 MFMA peak; HBM GB/s"
+HEADLINE_WORKLOAD = 2  # gemm_large_8192x8192x8192
+
+SHAPE_SEED = 2000  # inputs of a --shape run
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1,
-                    help="index into grouped_gemm_nvfp4_amd.inputs.WORKLOADS")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=HEADLINE_WORKLOAD,
+                    help="index into grouped_gemm_nvfp4_amd.inputs.WORKLOADS (default %d, the "
+                         "8192^3 product)" % HEADLINE_WORKLOAD)
     ap.add_argument("--shape", default=None, metavar="M,N,K",
                     help="time one GEMM of these sizes (seeded inputs, seed %d) instead of a "
                          "named workload" % SHAPE_SEED)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--copies", type=int, default=0,
                     help="operand copies to cycle over (0: enough to exceed the caches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0: skip)")
+    ap.add_argument("--clock-seconds", type=float, default=0.5,
+                    help="seconds of back-to-back headline steps during which the GPU clock is "
+                         "sampled (0: skip)")
     ap.add_argument("--scale-layout", choices=("plain", "blocked"), default="plain",
                     help="scales as [rows][K/16] (default) or in the pages' blocked 512-byte atoms "
                          "(nvfp4_gemm_blocked / nvfp4_group_gemm_blocked)")
@@ -78,14 +92,11 @@ def parse():
                          "the device (nvfp4_group_gemm_device: plan kernel + one-wave tiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 KERNEL_DIR = os.path.join(ROOT, "grouped_gemm_nvfp4_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-
-
-SHAPE_SEED = 2000  # inputs of a --shape run
 
 
 def parse_shape(text):
@@ -136,11 +147,20 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n, "launches": 5}))
 
 
+def affinity_cores():
+    """CPU cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count()
+
+
 def cpu_baseline(probs, target_s):
     """Time the oracle on a bounded sample of the workload, about target_s
     seconds of CPU work: the whole workload, repeated, when one pass is
     shorter than that; otherwise the leading rows of each problem's A with all
-    of N and K."""
+    of N and K.  ``cores`` is the number of threads the oracle ran on (its
+    OpenMP team: OMP_NUM_THREADS, else every core of the affinity mask)."""
     import oracle
 
     total_flops = inputs.flops([(p.M, p.N, p.K) for p in probs])
@@ -180,6 +200,7 @@ def cpu_baseline(probs, target_s):
                   "workload's flops, %.1f s" % (rows, done / total_flops, dt))
     return {"value": done / dt / 1e12, "unit": "TFLOPS", "cores": threads,
             "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+            "affinity_cores": affinity_cores(),
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
@@ -195,8 +216,297 @@ def cpu_model():
     return None
 
 
-def main():
-    args = parse()
+def rocm_version():
+    """The ROCm release of the image (/opt/rocm/.info/version), or None."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    try:
+        with open(os.path.join(rocm, ".info", "version")) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def sample_gfx_clock(run_step, seconds):
+    """Graphics clock (MHz, amdsmi) sampled every 10 ms from a helper thread
+    while the calling thread issues run_step() back to back for `seconds`.
+    Returns a summary dict, or one with an "error" when amdsmi is unusable."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:  # noqa: BLE001 - reporting only
+        return {"error": "amdsmi unavailable: %s" % (e,)}
+    samples, stop = [], threading.Event()
+    try:
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+
+        def sampler():
+            while not stop.is_set():
+                try:
+                    info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+                    samples.append(float(info["clk"]))
+                except Exception:  # noqa: BLE001
+                    pass
+                stop.wait(0.01)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            run_step(i)
+            i += 1
+            if i % 64 == 0:
+                import torch
+                torch.cuda.synchronize()
+        import torch
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+    if not samples:
+        return {"error": "no clock samples"}
+    # the first samples can predate the load: report the busy part
+    busy = samples[len(samples) // 5:] or samples
+    return {"window_s": seconds, "samples": len(samples),
+            "median_mhz": float(np.median(busy)), "min_mhz": float(np.min(busy)),
+            "max_mhz": float(np.max(busy))}
+
+
+class Bench:
+    """One workload's operands on the device (several copies), marshalled
+    calls, and its timing."""
+
+    def __init__(self, lib, g, b, wl, probs, seed, args):
+        import torch
+        self.lib, self.g, self.b = lib, g, b
+        self.wl, self.probs, self.seed = wl, probs, seed
+        self.shapes = [(p.M, p.N, p.K) for p in probs]
+        self.flops = inputs.flops(self.shapes)
+        self.alg_bytes = inputs.algorithmic_bytes(self.shapes)
+        self.blocked = args.scale_layout == "blocked"
+        self.pow2 = args.scales == "pow2"
+        self.device_table = args.table == "device" and wl.grouped
+        dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        sh = self.stream.cuda_stream
+
+        copies = args.copies or max(2, int(np.ceil(2 * CACHE_BYTES / self.alg_bytes)) + 1)
+        self.copies = min(copies, 64)
+        sets = []
+        host = [[torch.from_numpy(x) for x in (p.A, p.SFA, p.B, p.SFB)] for p in probs]
+        for _ in range(self.copies):
+            one = []
+            for p, h in zip(probs, host):
+                A, SFA, B, SFB = (x.to(dev) for x in h)
+                C = torch.empty((p.M, p.N), dtype=torch.float16, device=dev)
+                one.append((A, SFA, B, SFB, C))
+            sets.append(one)
+        if self.blocked:
+            # the scales of every copy moved into the blocked layout, on the
+            # device by the library itself
+            conv = []
+            for one in sets:
+                c1 = []
+                for (A, SFA, B, SFB, C), p in zip(one, probs):
+                    bsa = torch.empty(max(1, g.nvfp4_blocked_scale_bytes(p.M, p.K)), dtype=torch.uint8, device=dev)
+                    bsb = torch.empty(max(1, g.nvfp4_blocked_scale_bytes(p.N, p.K)), dtype=torch.uint8, device=dev)
+                    g.nvfp4_scales_to_blocked(SFA, bsa, p.M, p.K)
+                    g.nvfp4_scales_to_blocked(SFB, bsb, p.N, p.K)
+                    c1.append((A, bsa, B, bsb, C))
+                conv.append(c1)
+            torch.cuda.synchronize()
+            sets = conv
+        self.sets = sets
+
+        # marshal each set once; a step is then a single C call
+        calls = []
+        for one in sets:
+            if self.device_table:
+                rows = [(A, SFA, B, SFB, C, p.M, p.N, p.K) for (A, SFA, B, SFB, C), p in zip(one, probs)]
+                table = torch.frombuffer(bytearray(b.problem_table_bytes(rows)), dtype=torch.uint8).to(dev)
+                ws = torch.empty(g.nvfp4_group_gemm_device_workspace_bytes(len(one)), dtype=torch.uint8, device=dev)
+                tiles = sum(-(-p.M // 128) * -(-p.N // 128) for p in probs if p.M > 0 and p.N > 0)
+                calls.append(("device", (table.data_ptr(), len(one), tiles, ws.data_ptr(), ws.numel(), sh),
+                              (table, ws)))
+            elif not wl.grouped:
+                (A, SFA, B, SFB, C), p = one[0], probs[0]
+                calls.append(("gemm", (A.data_ptr(), SFA.data_ptr(), B.data_ptr(), SFB.data_ptr(),
+                                       C.data_ptr(), p.M, p.N, p.K, sh)))
+            else:
+                arr = (b.Nvfp4Problem * len(one))()
+                for i, ((A, SFA, B, SFB, C), p) in enumerate(zip(one, probs)):
+                    arr[i] = b.Nvfp4Problem(A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
+                                            SFB.data_ptr(), C.data_ptr(), p.M, p.N, p.K)
+                calls.append(("group", (arr, len(one), sh)))
+        self.calls = calls
+        self.gemm_fn = (lib.nvfp4_gemm_blocked if self.blocked else
+                        lib.nvfp4_gemm_pow2scale if self.pow2 else lib.nvfp4_gemm)
+        self.group_fn = (lib.nvfp4_group_gemm_blocked if self.blocked else
+                         lib.nvfp4_group_gemm_pow2scale if self.pow2 else lib.nvfp4_group_gemm)
+
+    def step(self, i):
+        kind, a = self.calls[i % len(self.calls)][:2]
+        rc = (self.gemm_fn(*a) if kind == "gemm" else self.group_fn(*a) if kind == "group"
+              else self.lib.nvfp4_group_gemm_device(*a))
+        if rc != 0:
+            raise RuntimeError(self.g.status_string(rc))
+
+    def plan(self):
+        """The library's plan of the call (host only)."""
+        if self.wl.grouped:
+            info, _ = self.g.group_gemm_plan(self.shapes)
+        else:
+            info = self.g.gemm_plan(*self.shapes[0])
+        return info
+
+    def run(self, steps, warmup):
+        """Time `steps` calls after `warmup` untimed ones.  Returns the timing
+        figures: wall clock of the timed region, the mean launch (HIP events on
+        the launch stream around the timed region, divided by the steps), a
+        per-launch event-pair distribution, the host time of one call and the
+        cache-warm mean launch (same operands every step)."""
+        import torch
+        stream = self.stream
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+
+        e_start = torch.cuda.Event(enable_timing=True)
+        e_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e_start.record(stream)
+        for i in range(steps):
+            self.step(i)
+        e_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_s = e_start.elapsed_time(e_end) / 1e3 / steps
+
+        nd = min(steps, 100)
+        d0 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+        d1 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
+        host = []
+        torch.cuda.synchronize()
+        for i in range(nd):
+            d0[i].record(stream)
+            h0 = time.perf_counter()
+            self.step(i)
+            host.append(time.perf_counter() - h0)
+            d1[i].record(stream)
+        torch.cuda.synchronize()
+        each_us = np.array([a.elapsed_time(z) for a, z in zip(d0, d1)]) * 1e3
+
+        torch.cuda.synchronize()
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        nwarm = min(steps, 50)
+        w0.record(stream)
+        for _ in range(nwarm):
+            self.step(0)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        warm_s = w0.elapsed_time(w1) / 1e3 / nwarm
+        return {"wall_s": wall, "kern_s": kern_s, "each_us": each_us,
+                "host_us": float(np.median(host)) * 1e6, "warm_s": warm_s}
+
+    def roofline(self, kern_s):
+        """Roofline object of the workload's kernel from its mean launch."""
+        kern_tflops = self.flops / kern_s / 1e12
+        kern_gbps = self.alg_bytes / kern_s / 1e9
+        single = not self.wl.grouped
+        traffic = None if (self.blocked or self.device_table or self.pow2) else measured_traffic(self.wl.name)
+        if single and self.probs[0].M <= 128 and self.flops / self.alg_bytes < 315:
+            # below the fp16 MFMA ridge (2.5 PFLOP/s / 8 TB/s): HBM-bound
+            roof = {"bound": "hbm", "achieved": kern_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": kern_gbps / PEAK_HBM_GBPS, "traffic": traffic}
+        elif self.pow2:
+            # the FP4-MFMA path: its own dtype's peak (fp4 x fp4 MFMA)
+            roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP4_TFLOPS,
+                    "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP4_TFLOPS, "traffic": traffic}
+        else:
+            roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS, "traffic": traffic}
+        return roof
+
+    def summary(self, t):
+        """Per-workload figures (used for the headline and for each extra)."""
+        kern_s = t["kern_s"]
+        kern_tflops = self.flops / kern_s / 1e12
+        roof = self.roofline(kern_s)
+        if self.alg_bytes < 2 ** 20:
+            roof["note"] = "latency-bound: too little work to reach either roofline"
+        roof["per_launch"] = {
+            "flops": self.flops, "algorithmic_bytes": self.alg_bytes,
+            "mean_launch_us": kern_s * 1e6,
+            "event_pair_us_p10_p50_p90": [float(np.percentile(t["each_us"], q)) for q in (10, 50, 90)],
+            "host_call_us_median": t["host_us"]}
+        return {
+            "workload": self.wl.name, "shapes_MNK": self.shapes, "seed": self.seed,
+            "operand_copies": self.copies, "plan": self.plan(),
+            "mean_launch_us": kern_s * 1e6, "kernel_tflops": kern_tflops,
+            "pct_fp16_peak": 100.0 * kern_tflops / PEAK_FP16_TFLOPS,
+            "pct_fp4_peak": 100.0 * kern_tflops / PEAK_FP4_TFLOPS,
+            "hbm_gbps": self.alg_bytes / kern_s / 1e9,
+            "roofline": roof,
+            "warm_cache_us": t["warm_s"] * 1e6,
+            "warm_cache_tflops": self.flops / t["warm_s"] / 1e12,
+        }
+
+    def release(self):
+        self.sets = None
+        self.calls = None
+
+
+def workload_spec(index, shape, codes):
+    """(Workload, problems, seed) of a named workload or a --shape product."""
+    if shape:
+        M, N, K = shape
+        wl = inputs.Workload("gemm_%dx%dx%d" % (M, N, K), False, "single GEMM M=%d N=%d K=%d" % (M, N, K))
+        return wl, inputs.draw_problems(SHAPE_SEED, [(M, N, K)], codes), SHAPE_SEED
+    wl = inputs.WORKLOADS[index]
+    return wl, inputs.draw_workload(index, codes), inputs.workload_shapes(index)[0]
+
+
+def compose(args, wl, seed, copies, flops, t, head, extras, cpu, system):
+    """The one JSON object bench.py prints."""
+    K = args.steps
+    return {
+        "metric": METRIC,
+        "value": flops * K / t["wall_s"] / 1e12,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": t["wall_s"] / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1" if args.scales == "pow2" else "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "shapes_MNK": head["shapes_MNK"], "seed": seed,
+                   "operand_copies": copies, "scale_layout": args.scale_layout,
+                   "scales": args.scales, "table": args.table, "plan": head["plan"]},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "pct_fp4_peak": head["pct_fp4_peak"],
+        "pct_fp16_peak": head["pct_fp16_peak"],
+        "hbm_gbps": head["hbm_gbps"],
+        "kernel_tflops": head["kernel_tflops"],
+        "warm_cache_us": head["warm_cache_us"],
+        "warm_cache_tflops": head["warm_cache_tflops"],
+        "workloads": extras,
+        "system": system,
+    }
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -204,196 +514,56 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    pow2 = args.scales == "pow2"
+    if pow2 and args.scale_layout != "plain":
+        print("--scales pow2 takes plain-layout scales only", file=sys.stderr)
+        sys.exit(2)
+    shape = parse_shape(args.shape) if args.shape else None
+    if not shape and not 0 <= args.workload < len(inputs.WORKLOADS):
+        print("--workload must be in 0..%d" % (len(inputs.WORKLOADS) - 1), file=sys.stderr)
+        sys.exit(2)
+    head_grouped = False if shape else inputs.WORKLOADS[args.workload].grouped
+    if args.table == "device" and (not head_grouped or args.scale_layout != "plain" or pow2):
+        print("--table device applies to grouped workloads with general plain-layout scales", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import grouped_gemm_nvfp4_amd as g
     from grouped_gemm_nvfp4_amd import _binding as b
 
     lib = g.load()
-    pow2 = args.scales == "pow2"
-    if pow2 and args.scale_layout != "plain":
-        print("--scales pow2 takes plain-layout scales only", file=sys.stderr)
-        sys.exit(2)
     codes = inputs.POW2_SCALE_CODES if pow2 else inputs.SCALE_CODES
-    if args.shape:
-        M, N, K = parse_shape(args.shape)
-        wl = inputs.Workload("gemm_%dx%dx%d" % (M, N, K), False, "single GEMM M=%d N=%d K=%d" % (M, N, K))
-        seed = SHAPE_SEED
-        probs = inputs.draw_problems(seed, [(M, N, K)], codes)
-    else:
-        wl = inputs.WORKLOADS[args.workload]
-        seed = inputs.workload_shapes(args.workload)[0]
-        probs = inputs.draw_workload(args.workload, codes)
-    shapes = [(p.M, p.N, p.K) for p in probs]
-    flops = inputs.flops(shapes)
-    alg_bytes = inputs.algorithmic_bytes(shapes)
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
 
-    copies = args.copies or max(2, int(np.ceil(2 * CACHE_BYTES / alg_bytes)) + 1)
-    copies = min(copies, 64)
-    sets = []
-    host = [[torch.from_numpy(x) for x in (p.A, p.SFA, p.B, p.SFB)] for p in probs]
-    for _ in range(copies):
-        one = []
-        for p, h in zip(probs, host):
-            A, SFA, B, SFB = (x.to(dev) for x in h)
-            C = torch.empty((p.M, p.N), dtype=torch.float16, device=dev)
-            one.append((A, SFA, B, SFB, C))
-        sets.append(one)
+    # the other named workloads first, each released before the next
+    extras = {}
+    if not shape and not args.no_extras:
+        for i, wl in enumerate(inputs.WORKLOADS):
+            if i == args.workload:
+                continue
+            wl_i, probs_i, seed_i = workload_spec(i, None, codes)
+            bi = Bench(lib, g, b, wl_i, probs_i, seed_i, args)
+            extras[wl_i.name] = bi.summary(bi.run(args.steps, args.warmup))
+            bi.release()
+            del bi
+            torch.cuda.empty_cache()
+            print("timed %s" % wl_i.name, file=sys.stderr, flush=True)
 
-    blocked = args.scale_layout == "blocked"
-    if blocked:
-        # the scales of every copy moved into the blocked layout, on the device
-        # by the library itself
-        conv = []
-        for one in sets:
-            c1 = []
-            for (A, SFA, B, SFB, C), p in zip(one, probs):
-                bsa = torch.empty(max(1, g.nvfp4_blocked_scale_bytes(p.M, p.K)), dtype=torch.uint8, device=dev)
-                bsb = torch.empty(max(1, g.nvfp4_blocked_scale_bytes(p.N, p.K)), dtype=torch.uint8, device=dev)
-                g.nvfp4_scales_to_blocked(SFA, bsa, p.M, p.K)
-                g.nvfp4_scales_to_blocked(SFB, bsb, p.N, p.K)
-                c1.append((A, bsa, B, bsb, C))
-            conv.append(c1)
-        torch.cuda.synchronize()
-        sets = conv
-
-    device_table = args.table == "device" and wl.grouped
-    if args.table == "device" and (not wl.grouped or blocked or pow2):
-        print("--table device applies to grouped workloads with general plain-layout scales", file=sys.stderr)
-        sys.exit(2)
-    # marshal each set once; a step is then a single C call
-    calls = []
-    for one in sets:
-        if device_table:
-            rows = [(A, SFA, B, SFB, C, p.M, p.N, p.K) for (A, SFA, B, SFB, C), p in zip(one, probs)]
-            table = torch.frombuffer(bytearray(b.problem_table_bytes(rows)), dtype=torch.uint8).to(dev)
-            ws = torch.empty(g.nvfp4_group_gemm_device_workspace_bytes(len(one)), dtype=torch.uint8, device=dev)
-            tiles = sum(-(-p.M // 128) * -(-p.N // 128) for p in probs if p.M > 0 and p.N > 0)
-            calls.append(("device", (table.data_ptr(), len(one), tiles, ws.data_ptr(), ws.numel(), sh),
-                          (table, ws)))
-            continue
-        if not wl.grouped:
-            (A, SFA, B, SFB, C), p = one[0], probs[0]
-            args_c = (A.data_ptr(), SFA.data_ptr(), B.data_ptr(), SFB.data_ptr(),
-                      C.data_ptr(), p.M, p.N, p.K, sh)
-            calls.append(("gemm", args_c))
-        else:
-            arr = (b.Nvfp4Problem * len(one))()
-            for i, ((A, SFA, B, SFB, C), p) in enumerate(zip(one, probs)):
-                arr[i] = b.Nvfp4Problem(A.data_ptr(), SFA.data_ptr(), B.data_ptr(),
-                                        SFB.data_ptr(), C.data_ptr(), p.M, p.N, p.K)
-            calls.append(("group", (arr, len(one), sh)))
-    gemm_fn = lib.nvfp4_gemm_blocked if blocked else lib.nvfp4_gemm_pow2scale if pow2 else lib.nvfp4_gemm
-    group_fn = (lib.nvfp4_group_gemm_blocked if blocked else
-                lib.nvfp4_group_gemm_pow2scale if pow2 else lib.nvfp4_group_gemm)
-
-    def step(i):
-        kind, a = calls[i % len(calls)][:2]
-        rc = (gemm_fn(*a) if kind == "gemm" else group_fn(*a) if kind == "group"
-              else lib.nvfp4_group_gemm_device(*a))
-        if rc != 0:
-            raise RuntimeError(g.status_string(rc))
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_start.record(stream)
-    for i in range(K):
-        step(i)
-    e_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_s = e_start.elapsed_time(e_end) / 1e3 / K
-
-    # per-launch distribution (a separate pass: an event pair around each
-    # call), and the host time of one call (enqueue only, no synchronisation)
-    nd = min(K, 100)
-    d0 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
-    d1 = [torch.cuda.Event(enable_timing=True) for _ in range(nd)]
-    host = []
-    torch.cuda.synchronize()
-    for i in range(nd):
-        d0[i].record(stream)
-        h0 = time.perf_counter()
-        step(i)
-        host.append(time.perf_counter() - h0)
-        d1[i].record(stream)
-    torch.cuda.synchronize()
-    each_us = np.array([a.elapsed_time(z) for a, z in zip(d0, d1)]) * 1e3
-    host_us = float(np.median(host)) * 1e6
-
-    # same operands every step (cache-warm), for context only
-    torch.cuda.synchronize()
-    w0 = torch.cuda.Event(enable_timing=True)
-    w1 = torch.cuda.Event(enable_timing=True)
-    nwarm = min(K, 50)
-    w0.record(stream)
-    for _ in range(nwarm):
-        step(0)
-    w1.record(stream)
-    torch.cuda.synchronize()
-    warm_s = w0.elapsed_time(w1) / 1e3 / nwarm
-
-    value = flops * K / wall / 1e12
-    kern_tflops = flops / kern_s / 1e12
-    kern_gbps = alg_bytes / kern_s / 1e9
-    small_m = (not wl.grouped) and probs[0].M <= 128
-    if small_m:
-        roof = {"bound": "hbm", "achieved": kern_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": kern_gbps / PEAK_HBM_GBPS,
-                "traffic": None if blocked else measured_traffic(wl.name)}
-    elif pow2:
-        # the FP4-MFMA path: its own dtype's peak (fp4 x fp4 MFMA)
-        roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP4_TFLOPS,
-                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP4_TFLOPS, "traffic": None}
-    else:
-        roof = {"bound": "mfma", "achieved": kern_tflops, "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": kern_tflops / PEAK_FP16_TFLOPS,
-                "traffic": None if blocked or device_table else measured_traffic(wl.name)}
-    roof["per_launch"] = {"flops": flops, "algorithmic_bytes": alg_bytes,
-                          "mean_launch_us": kern_s * 1e6,
-                          "event_pair_us_p10_p50_p90": [float(np.percentile(each_us, q)) for q in (10, 50, 90)],
-                          "host_call_us_median": host_us}
+    wl, probs, seed = workload_spec(args.workload, shape, codes)
+    bh = Bench(lib, g, b, wl, probs, seed, args)
+    t = bh.run(args.steps, args.warmup)
+    head = bh.summary(t)
+    clock = sample_gfx_clock(bh.step, args.clock_seconds) if args.clock_seconds > 0 else None
 
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(probs, args.cpu_seconds)
 
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "TFLOPS",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": wall / K * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "e2m1" if pow2 else "f16",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "description": wl.description,
-                   "shapes_MNK": shapes, "seed": seed,
-                   "operand_copies": copies, "scale_layout": args.scale_layout,
-                   "scales": args.scales, "table": args.table},
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "pct_fp4_peak": 100.0 * kern_tflops / PEAK_FP4_TFLOPS,
-        "pct_fp16_peak": 100.0 * kern_tflops / PEAK_FP16_TFLOPS,
-        "hbm_gbps": kern_gbps,
-        "kernel_tflops": kern_tflops,
-        "warm_cache_us": warm_s * 1e6,
-        "warm_cache_tflops": flops / warm_s / 1e12,
-    }
+    system = {"gpu": torch.cuda.get_device_name(0), "rocm": rocm_version(),
+              "torch_hip": getattr(torch.version, "hip", None),
+              "gfx_clock_under_headline_load": clock,
+              "affinity_cores": affinity_cores(),
+              "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+    out = compose(args, wl, seed, bh.copies, bh.flops, t, head, extras, cpu, system)
     print(json.dumps(out), flush=True)
 
 

@@ -5,6 +5,7 @@ the C ABI of include/nvfp4.h); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
     NVFP4_MAX_GROUPS,
+    NVFP4_MAX_K,
     Nvfp4Error,
     abi_version,
     gemm_plan,

@@ -18,6 +18,7 @@ NVFP4_ERROR_INVALID_VALUE = 1
 NVFP4_ERROR_NOT_SUPPORTED = 2
 NVFP4_ERROR_LAUNCH = 3
 NVFP4_MAX_GROUPS = 4096  # groups per grouped call
+NVFP4_MAX_K = 131072  # largest K of a product (the accuracy bound)
 
 EXPORTED = [
     "nvfp4_gemm", "nvfp4_group_gemm", "nvfp4_gemm_plan", "nvfp4_group_gemm_plan",

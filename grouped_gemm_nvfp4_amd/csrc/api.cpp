@@ -16,6 +16,8 @@
 #include <numeric>
 #include <queue>
 #include <mutex>
+#include <thread>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -28,9 +30,12 @@ using nvfp4::GroupTable;
 using nvfp4::kMaxGroupsPerLaunch;
 using nvfp4::TileConfig;
 
-// K beyond this would let a tile's buffer offsets leave the 31-bit range the
-// kernels' buffer loads use.
-constexpr int kMaxK = 1 << 24;
+// Largest K of a product: the accuracy bound (NVFP4_MAX_K in nvfp4.h).
+constexpr int kMaxK = NVFP4_MAX_K;
+static_assert(kMaxK == nvfp4::kMaxGemmK, "the device plan kernel checks the same limit");
+// Largest K of a scale-layout conversion: the conversions only move bytes;
+// beyond this a matrix's offsets would leave the 31-bit range of buffer loads.
+constexpr int kMaxScaleK = 1 << 24;
 // Workgroups per launch: gridDim.x * 256 threads must fit in 32 bits.
 constexpr long long kMaxWorkgroups = (0xffffffffll / 256);
 
@@ -90,12 +95,22 @@ long long list_makespan(const std::vector<std::pair<long long, long long>> &grou
 
 // Workspaces for K-split launches, one per (device, stream): work on one
 // stream runs in order, so a stream's calls never use its workspace
-// concurrently.  A buffer is only ever replaced by a larger one; replaced
-// buffers stay allocated (a captured graph may still refer to them) until
-// nvfp4_release_workspaces.
+// concurrently.  hipStreamPerThread names a different stream in every host
+// thread, so for it the calling thread is part of the key.  A buffer is only
+// ever replaced by a larger one; replaced buffers stay allocated (a captured
+// graph may still refer to them) until nvfp4_release_workspaces.
+struct WorkspaceKey {
+    int dev;
+    hipStream_t stream;
+    std::thread::id thread; // default-constructed unless stream is hipStreamPerThread
+    bool operator<(const WorkspaceKey &o) const
+    {
+        return std::tie(dev, stream, thread) < std::tie(o.dev, o.stream, o.thread);
+    }
+};
 struct Workspaces {
     std::mutex mu;
-    std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> live;
+    std::map<WorkspaceKey, std::pair<void *, size_t>> live;
     std::vector<std::pair<int, void *>> retired;
 };
 
@@ -115,7 +130,10 @@ nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
         return NVFP4_ERROR_LAUNCH;
     Workspaces &w = workspaces();
     std::lock_guard<std::mutex> lock(w.mu);
-    auto &e = w.live[std::make_pair(dev, stream)];
+    WorkspaceKey key{dev, stream, std::thread::id()};
+    if (stream == hipStreamPerThread)
+        key.thread = std::this_thread::get_id();
+    auto &e = w.live[key];
     if (e.first != nullptr && e.second >= bytes) {
         *out = e.first;
         return NVFP4_OK;
@@ -396,7 +414,7 @@ nvfp4_status check_scale_matrix(const void *a, const void *b, int rows, int K, c
 {
     if (rows < 0 || K < 0)
         return NVFP4_ERROR_INVALID_VALUE;
-    if (K % 32 != 0 || K > kMaxK)
+    if (K % 32 != 0 || K > kMaxScaleK)
         return NVFP4_ERROR_NOT_SUPPORTED;
     if (nvfp4::conv_workgroups(rows, K / 16) > 0x7fffffffLL)
         return NVFP4_ERROR_NOT_SUPPORTED;
@@ -651,7 +669,7 @@ nvfp4_status nvfp4_group_gemm_plan(const nvfp4_problem *problems, int num_groups
 
 long long nvfp4_blocked_scale_bytes(int rows, int K)
 {
-    if (rows < 0 || K < 0 || K % 32 != 0 || K > kMaxK)
+    if (rows < 0 || K < 0 || K % 32 != 0 || K > kMaxScaleK)
         return -1;
     return (long long)((rows + 127) / 128) * ((K / 16 + 3) / 4) * 512;
 }
@@ -701,7 +719,7 @@ nvfp4_status nvfp4_release_workspaces(void)
     };
     for (auto &kv : w.live)
         if (kv.second.first)
-            release(kv.first.first, kv.second.first);
+            release(kv.first.dev, kv.second.first);
     for (auto &r : w.retired)
         release(r.first, r.second);
     w.live.clear();
@@ -719,7 +737,7 @@ const char *nvfp4_status_string(nvfp4_status status)
     case NVFP4_ERROR_INVALID_VALUE:
         return "NVFP4_ERROR_INVALID_VALUE: null pointer, negative size or bad group count";
     case NVFP4_ERROR_NOT_SUPPORTED:
-        return "NVFP4_ERROR_NOT_SUPPORTED: K must be a multiple of 32 (at most 2^24), packed "
+        return "NVFP4_ERROR_NOT_SUPPORTED: K must be a multiple of 32 (at most NVFP4_MAX_K), packed "
                "operands 16-byte aligned, tile count within range";
     case NVFP4_ERROR_LAUNCH:
         return "NVFP4_ERROR_LAUNCH: a HIP launch or allocation failed";

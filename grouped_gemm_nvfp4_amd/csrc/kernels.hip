@@ -260,13 +260,20 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_tiled_kernel(GroupTable tab,
 // Last-arriver sum over the K slices of one output tile (split_k > 1).
 // Every workgroup of the tile stores its partial values (kN per thread, at
 // part + split * slice_elems + i * kStride) with agent-scope atomic stores,
-// which stay coherent across the chip's L2 caches without a whole-cache
-// write-back or invalidate; waits until they have completed; then takes a
-// ticket from the tile's counter.  The workgroup that draws the last ticket
-// adds the slices in slice order (so the result does not depend on arrival
-// order), returns true with the sums in v, and resets the counter to zero
-// for the next launch.  The others return false.  Every thread of the
+// then takes a ticket from the tile's counter.  The workgroup that draws the
+// last ticket adds the slices in slice order (so the result does not depend
+// on arrival order), returns true with the sums in v, and resets the counter
+// to zero for the next launch.  The others return false.  Every thread of the
 // workgroup must call it.
+//
+// Ordering (HIP / HSA memory model): the barrier makes every thread's partial
+// stores happen before thread 0's ticket, a fetch-add with release semantics
+// at agent scope.  The fetch-adds on one counter form a release sequence, so
+// the workgroup whose fetch-add returns S - 1 reads from every other
+// workgroup's release; its acquire fence (agent scope) then makes all their
+// partial stores visible to its loads after the second barrier.  The release
+// costs one L2 write-back per workgroup and the acquire one L2 invalidate per
+// output tile (last arriver only).
 template <int kN, int kStride>
 __device__ inline bool add_slices(float (&v)[kN], float *part, int slice_elems, int S, int split,
                                   int *counter, int *s_last)
@@ -275,10 +282,13 @@ __device__ inline bool add_slices(float (&v)[kN], float *part, int slice_elems, 
     for (int i = 0; i < kN; ++i)
         __hip_atomic_store(part + (long)split * slice_elems + i * kStride, v[i], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0)
-        *s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    if (threadIdx.x == 0) {
+        const bool last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        if (last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_last = last;
+    }
     __syncthreads();
     if (!*s_last)
         return false;

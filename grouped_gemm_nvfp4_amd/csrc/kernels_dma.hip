@@ -22,7 +22,7 @@ __global__ __launch_bounds__(64) void gemm_tiled_dma_dev_kernel(const uint8_t *w
 
 // Plan of a device-resident grouped call, one workgroup: each thread checks
 // up to four consecutive problems against the one-wave kernel's contract
-// (sizes >= 0, K % 128 == 0 and <= 2^24, pointers present, A and B 16-byte
+// (sizes >= 0, K % 128 == 0 and <= kMaxGemmK, pointers present, A and B 16-byte
 // and the scales 8-byte aligned, at most 2^24 tiles), writes their GemmDesc
 // and tile counts (zero when outside the contract or empty), and a
 // workgroup scan (64-bit, clamped to INT32_MAX) gives the exclusive prefix.
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_table_kernel(const P
         if (g >= G)
             break;
         const ProblemRecord p = problems[g];
-        bool ok = p.M >= 0 && p.N >= 0 && p.K >= 0 && p.K % 128 == 0 && p.K <= (1 << 24);
+        bool ok = p.M >= 0 && p.N >= 0 && p.K >= 0 && p.K % 128 == 0 && p.K <= kMaxGemmK;
         const bool empty = p.M == 0 || p.N == 0;
         long long tiles = 0;
         if (ok && !empty) {

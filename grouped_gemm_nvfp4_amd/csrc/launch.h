@@ -21,6 +21,9 @@ struct GemmDesc {
     int tiles_m;        // ceil(M / tile_m)
 };
 
+// Largest K of a product (NVFP4_MAX_K of the C ABI): the accuracy bound.
+constexpr int kMaxGemmK = 1 << 17;
+
 // Groups per launch.  The table below stays under the 4 KiB kernel-argument
 // budget; a call with more groups is issued as several launches.
 constexpr int kMaxGroupsPerLaunch = 64;

@@ -29,9 +29,19 @@
  * the boundary.  Argument errors are reported before any HIP call is made.
  *
  * Threads: the calls may be made from several threads.  Calls that split K
- * use a device workspace that the library keeps per (device, stream) pair and
- * grows on demand (hipMalloc, outside the enqueued work); calls on one stream
- * are ordered by that stream, so they never share a workspace concurrently.
+ * use a device workspace that the library keeps per (device, stream) pair
+ * (per calling thread as well for hipStreamPerThread) and grows on demand
+ * (hipMalloc plus a clear of its tile counters, both outside the enqueued
+ * work); calls on one stream are ordered by that stream, so they never share
+ * a workspace concurrently.
+ *
+ * Stream capture: a call that would have to allocate or grow its stream's
+ * workspace while that stream is capturing returns NVFP4_ERROR_NOT_SUPPORTED
+ * and enqueues nothing; one eager call of the same or a larger size on the
+ * stream beforehand makes the captured call possible.  A captured K-split
+ * call keeps using the workspace of the stream it was captured on: its graph
+ * must not run at the same time as other work that uses that workspace (eager
+ * calls on that stream, or other replays of graphs captured on it).
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -45,6 +55,13 @@ extern "C" {
 #define NVFP4_ABI_VERSION 1
 /* Largest number of groups a single grouped call accepts. */
 #define NVFP4_MAX_GROUPS 4096
+/* Largest K of a product.  The kernels accumulate in fp32; an output's
+ * longest serial chain is K / 16 matrix-core steps plus at most a few dozen
+ * sums of partial results.  Counting two roundings per step, each at most
+ * 2^-24 of a partial sum no larger than sum_k |a_k b_k|, the accumulated error
+ * stays below K * 2^-27 * sum_k |a_k b_k| + 2^-19 * sum_k |a_k b_k|, which is
+ * inside the 1e-3 * sum_k |a_k b_k| accuracy bound for every K up to this. */
+#define NVFP4_MAX_K 131072
 
 typedef enum {
     NVFP4_OK = 0,
@@ -70,7 +87,7 @@ typedef struct {
  *   K == 0: C is filled with +0 (the empty sum).
  * Errors: any pointer NULL while M*N > 0 (A/SFA/B/SFB only when K > 0)
  *   -> NVFP4_ERROR_INVALID_VALUE; negative sizes -> INVALID_VALUE;
- *   K % 32 != 0, K > 2^24, A or B not 16-byte aligned, or more than
+ *   K % 32 != 0, K > NVFP4_MAX_K, A or B not 16-byte aligned, or more than
  *   2^24 - 1 workgroups -> NVFP4_ERROR_NOT_SUPPORTED;
  *   a failed launch or workspace allocation -> NVFP4_ERROR_LAUNCH.
  */
@@ -123,7 +140,7 @@ nvfp4_status nvfp4_gemm_batched(const void *A, const void *SFA, const void *B, c
  * memset: the call can be captured in a HIP graph.
  *
  * Per-entry contract, checked on the device: M, N, K >= 0; K % 128 == 0 and
- * K <= 2^24; when M N > 0, C present and, when K > 0, A, SFA, B, SFB present
+ * K <= NVFP4_MAX_K; when M N > 0, C present and, when K > 0, A, SFA, B, SFB present
  * with A and B 16-byte and SFA and SFB 8-byte aligned; at most 2^24 tiles.
  * An entry outside it gets no tiles (its C is not written) and is counted.
  * After the work has run, the workspace starts with four int32: num_groups,

@@ -40,6 +40,7 @@ def test_binding_constants_match_header():
     text = open(HEADER).read()
     defines = dict(re.findall(r"#define (NVFP4_[A-Z_]+) (-?\d+)", text))
     assert int(defines["NVFP4_MAX_GROUPS"]) == g.NVFP4_MAX_GROUPS
+    assert int(defines["NVFP4_MAX_K"]) == g.NVFP4_MAX_K
     assert int(defines["NVFP4_ABI_VERSION"]) == g.abi_version()
     for name in ("NVFP4_OK", "NVFP4_ERROR_INVALID_VALUE", "NVFP4_ERROR_NOT_SUPPORTED", "NVFP4_ERROR_LAUNCH"):
         m = re.search(name + r"\s*=\s*(\d+)", text)
@@ -61,6 +62,7 @@ ALIGNED = 1 << 20  # stand-in device address: never dereferenced by these calls
     (4, 4, -32, b.NVFP4_ERROR_INVALID_VALUE),
     (4, 4, 48, b.NVFP4_ERROR_NOT_SUPPORTED),
     (4, 4, 16, b.NVFP4_ERROR_NOT_SUPPORTED),
+    (4, 4, b.NVFP4_MAX_K + 32, b.NVFP4_ERROR_NOT_SUPPORTED),
     (4, 4, (1 << 24) + 32, b.NVFP4_ERROR_NOT_SUPPORTED),
     (1 << 30, 1 << 30, 32, b.NVFP4_ERROR_NOT_SUPPORTED),
 ])
@@ -285,3 +287,19 @@ def test_problem_table_bytes_layout():
     words = np.frombuffer(raw[:56], dtype=np.uint64)[:5]
     assert list(words) == [16, 32, 48, 64, 80]
     assert list(np.frombuffer(raw[40:52], dtype=np.int32)) == [1, 2, 128]
+
+
+def test_k_limit_is_the_accuracy_bound():
+    """K up to NVFP4_MAX_K plans; one block of 32 more is refused, by the
+    plain, blocked and power-of-two entry points alike."""
+    K = g.NVFP4_MAX_K
+    assert g.gemm_plan(64, 64, K)["workgroups"] > 0
+    assert g.gemm_plan(256, 16512, K)["tile_m"] == 128
+    for fn in (b.raw_gemm,):
+        assert fn(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 4, 4, K + 32, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    lib = g.load()
+    for name in ("nvfp4_gemm_blocked", "nvfp4_gemm_pow2scale"):
+        fn = getattr(lib, name)
+        assert fn(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 4, 4, K + 128, None) == b.NVFP4_ERROR_NOT_SUPPORTED
+    # the worst-case accumulated error bound at the limit, as nvfp4.h states it
+    assert K * 2.0 ** -27 + 2.0 ** -19 < 1e-3

@@ -44,3 +44,87 @@ def test_shape_option_parsing():
     for bad in ("64,4096", "64,4096,70", "0,8,32", "a,b,c"):
         with pytest.raises(SystemExit):
             bench.parse_shape(bad)
+
+
+def test_default_headline_is_the_large_workload():
+    args = bench.parse([])
+    assert args.workload == bench.HEADLINE_WORKLOAD
+    assert inputs.WORKLOADS[args.workload].name == "gemm_large_8192x8192x8192"
+    assert args.gpus == 1 and not args.no_extras
+
+
+def _fake_bench(index):
+    """A Bench with its host-side fields set, as the GPU run would set them."""
+    wl = inputs.WORKLOADS[index]
+    _, shapes = inputs.workload_shapes(index)
+    b = object.__new__(bench.Bench)
+    b.wl, b.shapes, b.seed, b.copies = wl, shapes, 1000 + index, 3
+    b.probs = [inputs.Problem(M, N, K, None, None, None, None) for (M, N, K) in shapes]
+    b.flops = inputs.flops(shapes)
+    b.alg_bytes = inputs.algorithmic_bytes(shapes)
+    b.blocked = b.pow2 = b.device_table = False
+    b.plan = lambda: {"kernel": 1}
+    return b
+
+
+def _fake_timing(kern_us):
+    import numpy as np
+    return {"wall_s": kern_us * 1e-6 * 20 * 1.05, "kern_s": kern_us * 1e-6,
+            "each_us": np.full(20, kern_us), "host_us": 5.0, "warm_s": kern_us * 0.9e-6}
+
+
+def test_output_line_carries_every_field():
+    """The JSON line of a run: the driver's contract, the roofline and CPU
+    baseline objects, the other workloads and the system metadata."""
+    args = bench.parse(["--steps", "20", "--warmup", "5"])
+    heads = {}
+    extras = {}
+    for i in range(len(inputs.WORKLOADS)):
+        fb = _fake_bench(i)
+        s = fb.summary(_fake_timing(900.0 if i == 2 else 30.0))
+        if i == args.workload:
+            heads = (fb, s)
+        else:
+            extras[fb.wl.name] = s
+    fb, head = heads
+    cpu = {"value": 0.04, "unit": "TFLOPS", "cores": 16, "kind": "oracle", "sample": "x",
+           "affinity_cores": 16, "omp_num_threads": "16"}
+    system = {"gpu": "x", "rocm": bench.rocm_version(), "torch_hip": None,
+              "gfx_clock_under_headline_load": {"median_mhz": 1700.0},
+              "affinity_cores": bench.affinity_cores(), "omp_num_threads": None}
+    out = bench.compose(args, fb.wl, fb.seed, fb.copies, fb.flops, _fake_timing(900.0), head, extras,
+                        cpu, system)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline", "pct_fp4_peak", "pct_fp16_peak", "workloads", "system"):
+        assert key in out, key
+    assert out["config"]["workload"] == "gemm_large_8192x8192x8192"
+    assert out["dtype"] == "f16" and out["n_gpus"] == 1 and out["vs_baseline"] is None
+    roof = out["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
+    assert abs(roof["frac"] - fb.flops / 900e-6 / 1e12 / 2500.0) < 1e-12
+    assert set(out["workloads"]) == {w.name for w in inputs.WORKLOADS} - {"gemm_large_8192x8192x8192"}
+    small = out["workloads"]["gemm_smallM_64x7168x16384"]
+    assert small["roofline"]["bound"] == "hbm" and small["roofline"]["unit"] == "GB/s"
+    for s in out["workloads"].values():
+        for key in ("mean_launch_us", "kernel_tflops", "pct_fp16_peak", "pct_fp4_peak", "hbm_gbps",
+                    "roofline", "plan"):
+            assert key in s
+        assert "frac" in s["roofline"] and "traffic" in s["roofline"]
+    assert out["workloads"]["gemm_128x128x256"]["roofline"].get("note", "").startswith("latency")
+    for key in ("gpu", "rocm", "gfx_clock_under_headline_load", "affinity_cores", "omp_num_threads"):
+        assert key in out["system"]
+    assert out["cpu_baseline"]["cores"] >= 1 and "affinity_cores" in out["cpu_baseline"]
+
+
+def test_clock_sampler_reports_without_a_gpu():
+    """Without a usable GPU the clock sampler returns an error record instead
+    of raising (the bench line still prints)."""
+    r = bench.sample_gfx_clock(lambda i: None, 0.01)
+    assert isinstance(r, dict) and ("error" in r or "median_mhz" in r)
+
+
+def test_metadata_helpers():
+    assert bench.affinity_cores() >= 1
+    v = bench.rocm_version()
+    assert v is None or v[0].isdigit()

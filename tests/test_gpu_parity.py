@@ -3,8 +3,10 @@
 Rule (tests/parity.py): |gpu - C16| <= 1e-3 * sum_k |a_k b_k| + ulp16(C16).
 Every output buffer is poisoned with 0xFFFF (a NaN) before the call, so an
 element the kernel fails to write shows up as a failure.  Small and medium
-shapes are compared in full; the full-size workloads are compared on sampled
-outputs (whole rows and columns at tile edges plus random entries), which the
+shapes and all five named workloads at full size are compared in full.  The
+few shapes too large for a quick full oracle product are compared on sampled
+outputs (whole rows and columns at the edges of the tiles the plan runs, the
+last row and column always among them, plus random entries), which the
 oracle computes one by one, and checked in full for unwritten elements.
 """
 import numpy as np
@@ -58,16 +60,32 @@ def check_full(lib, p, what):
     return got, c16
 
 
-def sample_positions(rng, M, N, tile=128, n_random=3000):
+def edge_indices(L, tile):
+    """Indices along one output dimension of length L where tile edges and
+    masking act: the first and last index, the first index of the last tile,
+    and both sides of every tile boundary."""
+    s = {0, L - 1, ((L - 1) // tile) * tile}
+    for e in range(tile - 1, L, tile):
+        s |= {e, min(L - 1, e + 1)}
+    return sorted(s)
+
+
+def pick_edges(xs, n=12):
+    """At most about n of the sorted edge indices: always the first two and
+    the last three (the ragged tail), plus an even spread of the rest."""
+    step = max(1, len(xs) // max(1, n - 5))
+    return sorted(set(xs[:2] + xs[-3:] + xs[::step]))
+
+
+def sample_positions(rng, M, N, tile_m=128, tile_n=128, n_random=3000):
+    """Whole rows and whole columns at the tile edges of the plan that runs
+    (first, last, the last tile's first, around internal boundaries), plus
+    n_random random outputs."""
     rows, cols = [], []
-    edge_rows = sorted({0, M - 1} | {min(M - 1, t) for t in range(tile - 1, M, tile)}
-                       | {min(M - 1, t + 1) for t in range(tile - 1, M, tile)})
-    edge_cols = sorted({0, N - 1} | {min(N - 1, t) for t in range(tile - 1, N, tile)}
-                       | {min(N - 1, t + 1) for t in range(tile - 1, N, tile)})
-    for r in edge_rows[:6]:
+    for r in pick_edges(edge_indices(M, tile_m)):
         rows += [r] * N
         cols += list(range(N))
-    for c in edge_cols[:6]:
+    for c in pick_edges(edge_indices(N, tile_n)):
         rows += list(range(M))
         cols += [c] * M
     rows += list(rng.integers(0, M, n_random))
@@ -75,12 +93,24 @@ def sample_positions(rng, M, N, tile=128, n_random=3000):
     return np.array(rows), np.array(cols)
 
 
-def check_sampled(got, p, seed, what):
+def plan_tile(lib, M, N, K):
+    info = lib.gemm_plan(M, N, K)
+    return info["tile_m"], info["tile_n"]
+
+
+def check_sampled(got, p, seed, what, tile=(128, 128)):
     assert not np.any(got == 0xFFFF), "%s: unwritten (poisoned) outputs remain" % what
     rng = np.random.default_rng(seed)
-    rows, cols = sample_positions(rng, p.M, p.N)
+    rows, cols = sample_positions(rng, p.M, p.N, tile[0], tile[1])
     c16, _, bound = oracle.gemm_entries(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K, rows, cols)
     assert_parity(got[rows, cols], c16, bound, what)
+
+
+def check_against_full_oracle(got, p, what):
+    """Every output against the oracle's full product (and none left
+    unwritten: the poison is a NaN, which never passes)."""
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+    assert_parity(got, c16, bound, what)
 
 
 # ------------------------------------------------------------------ single GEMM
@@ -123,7 +153,7 @@ def test_tiled_variants(lib, M, N, K, kernel):
         check_full(lib, p, "tiled %dx%dx%d" % (M, N, K))
     else:
         got = run_gemm(lib, p)
-        check_sampled(got, p, 91, "tiled %dx%dx%d" % (M, N, K))
+        check_sampled(got, p, 91, "tiled %dx%dx%d" % (M, N, K), plan_tile(lib, M, N, K))
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -137,7 +167,7 @@ def test_one_wave_tiles_scale_loads(lib, M, N, K):
     assert info["kernel"] == 1 and info["tile_m"] == 128
     p = inputs.draw_problems(4100 + K, [(M, N, K)])[0]
     got = run_gemm(lib, p)
-    check_sampled(got, p, 4101 + K, "one-wave %dx%dx%d" % (M, N, K))
+    check_sampled(got, p, 4101 + K, "one-wave %dx%dx%d" % (M, N, K), plan_tile(lib, M, N, K))
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -154,7 +184,7 @@ def test_four_wave_direct_tiles(lib, M, N, K):
     assert info["kernel"] == 3 and info["tile_m"] == 128
     p = inputs.draw_problems(4200 + K, [(M, N, K)])[0]
     got = run_gemm(lib, p)
-    check_sampled(got, p, 4201 + K, "four-wave %dx%dx%d" % (M, N, K))
+    check_sampled(got, p, 4201 + K, "four-wave %dx%dx%d" % (M, N, K), plan_tile(lib, M, N, K))
     assert np.array_equal(got, run_gemm(lib, p)), "four-wave sums must not depend on timing"
 
 
@@ -231,7 +261,7 @@ def test_random_shapes_across_planner_regimes(lib, M, N, K):
     if M * N <= 300_000:
         check_full(lib, p, "random %dx%dx%d" % (M, N, K))
     else:
-        check_sampled(run_gemm(lib, p), p, 9101 + N, "random %dx%dx%d" % (M, N, K))
+        check_sampled(run_gemm(lib, p), p, 9101 + N, "random %dx%dx%d" % (M, N, K), plan_tile(lib, M, N, K))
 
 
 def test_few_tiles_deterministic(lib):
@@ -310,9 +340,37 @@ def test_overflow_gives_infinity(lib):
 
 @pytest.mark.parametrize("index", [1, 2])
 def test_full_size_single_workloads(lib, index):
+    """The small-M (64 x 7168 x 16384) and large (8192^3) workloads at full
+    size, in the launch configuration bench.py times, every output against the
+    oracle's full product."""
     (p,) = inputs.draw_workload(index)
     got = run_gemm(lib, p)
-    check_sampled(got, p, 50 + index, inputs.WORKLOADS[index].name)
+    check_against_full_oracle(got, p, inputs.WORKLOADS[index].name)
+
+
+@pytest.mark.parametrize("M,N,kernel_tile", [
+    (4, 64, 64),       # 64-row kernels: K split across eight waves and the workgroups
+    (256, 16512, 128), # 258 one-wave 128 x 128 tiles: one serial chain over all of K
+])
+def test_largest_k_all_positive(lib, M, N, kernel_tile):
+    """K at the library's limit (NVFP4_MAX_K = 131072) with every term
+    positive, so every partial sum is as large as the final one: the case where
+    fp32 rounding, relative to the bound sum_k |a_k b_k|, is largest.  The
+    parity tolerance must still hold there."""
+    K = 131072
+    info = lib.gemm_plan(M, N, K)
+    assert info["tile_m"] == kernel_tile
+    rng = np.random.default_rng(6000 + M)
+    p = inputs.draw_problems(6000 + M, [(M, N, K)])[0]
+    # positive e2m1 codes only: clear the sign bit of both nibbles
+    p.A &= 0x77
+    p.B &= 0x77
+    got = run_gemm(lib, p)
+    if M * N <= 1 << 16:
+        check_against_full_oracle(got, p, "K=%d all positive %dx%d" % (K, M, N))
+    else:
+        check_sampled(got, p, int(rng.integers(1 << 30)), "K=%d all positive %dx%d" % (K, M, N),
+                      plan_tile(lib, M, N, K))
 
 
 # ------------------------------------------------------------------ grouped GEMM
@@ -478,10 +536,12 @@ def test_group_split_k_across_launches(lib, kernel_tile_n, max_n):
 
 @pytest.mark.parametrize("index", [3, 4])
 def test_full_size_grouped_workloads(lib, index):
+    """The 8-group MoE-like and 2-group workloads at full size, as bench.py
+    runs them, every output of every group against the oracle."""
     probs = inputs.draw_workload(index)
     outs = run_group(lib, probs)
     for gi, (p, got) in enumerate(zip(probs, outs)):
-        check_sampled(got, p, 60 + 10 * index + gi, "%s group %d" % (inputs.WORKLOADS[index].name, gi))
+        check_against_full_oracle(got, p, "%s group %d" % (inputs.WORKLOADS[index].name, gi))
 
 
 def test_grouped_workload_reduced_full_compare(lib):
@@ -771,3 +831,46 @@ def test_group_gemm_device_table_in_graph(lib):
                 continue
             c16, _, bound = oracle.gemm(p.A[:m], p.SFA[:m], p.B, p.SFB, m, N, K)
             assert_parity(got[:m], c16, bound, "graph replay M=%s group %d" % (ms, g_))
+
+
+def test_k_split_gemm_under_stream_capture(lib):
+    """A K-split call needs its stream's workspace.  Captured on a stream that
+    has none yet it is refused (NOT_SUPPORTED, nothing enqueued); after one
+    eager call on that stream the same call captures, and every replay of the
+    graph (eager work and synchronisations between them) matches the oracle."""
+    M, N, K = 64, 1024, 8192
+    info = lib.gemm_plan(M, N, K)
+    assert info["split_k"] > 1 and info["workspace_bytes"] > 0
+    p = inputs.draw_problems(6100, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    torch.cuda.synchronize()
+    assert lib.release_workspaces() is None  # no stream has a workspace now
+    s = torch.cuda.Stream()
+    args = (A.data_ptr(), SFA.data_ptr(), B.data_ptr(), SFB.data_ptr(), C.data_ptr(), M, N, K)
+    from grouped_gemm_nvfp4_amd import _binding as b
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        rc = b.raw_gemm(*args, s.cuda_stream)
+    assert rc == b.NVFP4_ERROR_NOT_SUPPORTED
+    torch.cuda.synchronize()
+    assert np.all(bits(C) == 0xFFFF), "a refused call enqueued nothing"
+    del graph
+
+    with torch.cuda.stream(s):
+        assert b.raw_gemm(*args, s.cuda_stream) == b.NVFP4_OK  # allocates the workspace
+    torch.cuda.synchronize()
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(bits(C), c16, bound, "eager K-split call")
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        rc = b.raw_gemm(*args, s.cuda_stream)
+    assert rc == b.NVFP4_OK
+    for rep in range(3):
+        C.fill_(-1)
+        x = torch.ones(1 << 20, device="cuda")  # unrelated eager work between replays
+        x.mul_(2.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_parity(bits(C), c16, bound, "K-split graph replay %d" % rep)
