@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     nvfp4_gemm,
     nvfp4_gemm_batched,
     nvfp4_gemm_blocked,
+    nvfp4_gemm_noalloc,
     nvfp4_gemm_pow2scale,
     nvfp4_group_gemm,
     nvfp4_group_gemm_blocked,

@@ -27,6 +27,7 @@ EXPORTED = [
     "nvfp4_gemm_blocked", "nvfp4_group_gemm_blocked",
     "nvfp4_gemm_pow2scale", "nvfp4_group_gemm_pow2scale",
     "nvfp4_gemm_batched", "nvfp4_group_gemm_device_workspace_bytes", "nvfp4_group_gemm_device",
+    "nvfp4_gemm_noalloc",
 ]
 
 
@@ -100,6 +101,8 @@ def load():
     lib.nvfp4_group_gemm_device.argtypes = [vp, ci, ci, vp, ctypes.c_longlong, vp]
     lib.nvfp4_group_gemm_device.restype = ci
     lib.nvfp4_gemm_pow2scale.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.nvfp4_gemm_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, vp]
+    lib.nvfp4_gemm_noalloc.restype = ci
     lib.nvfp4_gemm_pow2scale.restype = ci
     lib.nvfp4_group_gemm_pow2scale.argtypes = [ctypes.POINTER(Nvfp4Problem), ci, vp]
     lib.nvfp4_group_gemm_pow2scale.restype = ci
@@ -241,6 +244,20 @@ def nvfp4_scales_from_blocked(blocked, sf, rows, K, stream=None):
 def raw_gemm(A, SFA, B, SFB, C, M, N, K, stream) -> int:
     """The C entry point with raw integer pointers; returns the status code."""
     return load().nvfp4_gemm(A, SFA, B, SFB, C, M, N, K, stream)
+
+
+def raw_gemm_noalloc(A, SFA, B, SFB, C, M, N, K, stream) -> int:
+    """nvfp4_gemm_noalloc with raw integer pointers; returns the status code."""
+    return load().nvfp4_gemm_noalloc(A, SFA, B, SFB, C, M, N, K, stream)
+
+
+def nvfp4_gemm_noalloc(A, SFA, B, SFB, C, M=None, N=None, K=None, stream=None):
+    """nvfp4_gemm without any device allocation (K-split scratch in the
+    library's per-GPU static array); raises Nvfp4Error on a bad status."""
+    if M is None:
+        M, N, K = _sizes(A, B, C)
+    _check(load().nvfp4_gemm_noalloc(_ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _ptr(C),
+                                     M, N, K, _stream_handle(stream)))
 
 
 def raw_group_gemm(problems, num_groups, stream) -> int:

@@ -350,15 +350,12 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
     info->workspace_bytes = plan.workspace_bytes;
 }
 
-// Launches a finished plan: groups in plan order, kMaxGroupsPerLaunch per
+// Launches a finished plan with its workspace (plan.workspace_bytes at
+// `workspace`, counters zero): groups in plan order, kMaxGroupsPerLaunch per
 // launch.
-nvfp4_status run_plan(const nvfp4_problem *problems, const Plan &plan, hipStream_t stream)
+nvfp4_status launch_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
 {
-    void *workspace = nullptr;
-    nvfp4_status s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
-    if (s != NVFP4_OK)
-        return s;
-
+    nvfp4_status s = NVFP4_OK;
     GroupTable table;
     memset(&table, 0, sizeof(table));
     table.split_k = plan.split_k;
@@ -397,6 +394,16 @@ nvfp4_status run_plan(const nvfp4_problem *problems, const Plan &plan, hipStream
         }
     }
     return flush();
+}
+
+// Launches a finished plan in its stream's library-owned workspace.
+nvfp4_status run_plan(const nvfp4_problem *problems, const Plan &plan, hipStream_t stream)
+{
+    void *workspace = nullptr;
+    nvfp4_status s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
+    if (s != NVFP4_OK)
+        return s;
+    return launch_plan(problems, plan, workspace, stream);
 }
 
 nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream, bool pow2 = false)
@@ -527,9 +534,84 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
     return run(plain.data(), num_groups, stream);
 }
 
+// ------------------------------------------------- allocation-free variant
+//
+// nvfp4_gemm_noalloc: the plan and kernels of nvfp4_gemm, with the K-split
+// workspace in this file-scope device array instead of a library-allocated
+// buffer.  Each GPU that runs the library holds its own copy until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, taken once per device (with
+// that device current) on the entry point's first call there.
+constexpr long long kScratchBytes = nvfp4::kCounterBytes + 4LL * 1024 * 1024;
+static_assert(kScratchBytes == NVFP4_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchAddresses {
+    std::mutex mu;
+    std::map<int, void *> per_device;
+};
+
+ScratchAddresses &scratch_addresses()
+{
+    static ScratchAddresses *s = new ScratchAddresses(); // never destroyed: usable at exit
+    return *s;
+}
+
+nvfp4_status device_scratch(void **out)
+{
+    *out = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return NVFP4_ERROR_LAUNCH;
+    ScratchAddresses &s = scratch_addresses();
+    std::lock_guard<std::mutex> lock(s.mu);
+    auto it = s.per_device.find(dev);
+    if (it != s.per_device.end()) {
+        *out = it->second;
+        return NVFP4_OK;
+    }
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+        return NVFP4_ERROR_LAUNCH;
+    s.per_device[dev] = ptr;
+    *out = ptr;
+    return NVFP4_OK;
+}
+
 } // namespace
 
 extern "C" {
+
+nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, const void *SFB, void *C, int M,
+                                int N, int K, hipStream_t stream)
+{
+    nvfp4_problem p;
+    p.A = A;
+    p.SFA = SFA;
+    p.B = B;
+    p.SFB = SFB;
+    p.C = C;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    Plan plan;
+    nvfp4_status s = make_plan(&p, 1, &plan);
+    if (s != NVFP4_OK || plan.total_tiles == 0)
+        return s;
+    if (plan.workspace_bytes > kScratchBytes)
+        return NVFP4_ERROR_NOT_SUPPORTED;
+    void *ws = nullptr;
+    if (plan.workspace_bytes > 0) {
+        s = device_scratch(&ws);
+        if (s != NVFP4_OK)
+            return s;
+        // the tile counters start at zero: a kernel clears them (no memset
+        // node in a captured graph), ordered before the GEMM by the stream
+        if (nvfp4::launch_clear_words(ws, (int)(nvfp4::kCounterBytes / 4), stream) != hipSuccess)
+            return NVFP4_ERROR_LAUNCH;
+    }
+    return launch_plan(&p, plan, ws, stream);
+}
 
 nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const void *SFB,
                         void *C, int M, int N, int K, hipStream_t stream)

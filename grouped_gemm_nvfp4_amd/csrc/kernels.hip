@@ -926,7 +926,22 @@ __global__ __launch_bounds__(256) void scale_conversion_kernel(ScaleConvTable ta
     }
 }
 
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *p, int words)
+{
+    for (int i = (int)threadIdx.x; i < words; i += 256)
+        p[i] = 0;
+}
+
 } // namespace
+
+hipError_t launch_clear_words(void *p, int words, hipStream_t stream)
+{
+    if (words <= 0)
+        return hipSuccess;
+    uint32_t *q = (uint32_t *)p;
+    void *args[] = {&q, &words};
+    return hipLaunchKernel((const void *)clear_words_kernel, dim3(1), dim3(256), args, 0, stream);
+}
 
 hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, hipStream_t stream)
 {

@@ -159,4 +159,7 @@ inline long long conv_workgroups(int rows, int kb)
 
 hipError_t launch_scale_conversion(const ScaleConvTable &table, hipStream_t stream);
 
+// Sets `words` 32-bit words at p to zero with a kernel (one workgroup).
+hipError_t launch_clear_words(void *p, int words, hipStream_t stream);
+
 } // namespace nvfp4

@@ -227,6 +227,24 @@ nvfp4_status nvfp4_gemm_pow2scale(const void *A, const void *SFA, const void *B,
 nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_groups,
                                         hipStream_t stream);
 
+/* ---- Allocation-free single GEMM.  For callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, layouts, results (bitwise those of
+ * nvfp4_gemm) and errors as nvfp4_gemm, with the same plan and kernels; the
+ * calls that split K keep their tile counters and partial sums in a scratch
+ * array of NVFP4_NOALLOC_SCRATCH_BYTES bytes that the library holds in device
+ * memory on each GPU it runs on, until the process ends.  The call allocates
+ * nothing (no hipMalloc, no library or torch allocation) and enqueues a small
+ * kernel that clears the counters before the product, so it can be captured
+ * on any stream.  Every call on a GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, concurrent graph replays) race
+ * and give wrong results.  A plan whose workspace would exceed the array
+ * returns NVFP4_ERROR_NOT_SUPPORTED (the planner keeps K-split launches at
+ * 256 workgroups of at most 16 KiB of partial sums, within it). */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (16384 + 4194304)
+nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, const void *SFB,
+                                void *C, int M, int N, int K, hipStream_t stream);
+
 /* How a call would be carried out (host only, no HIP call).  For tests and
  * reports. */
 typedef struct {
