@@ -16,7 +16,7 @@ INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libnvfp4.so")
 
 SOURCES = ["api.cpp", "kernels.hip", "kernels_dma.hip", "kernels_dma_one.hip", "kernels_dma_special.hip",
-           "kernels_dma_four.hip"]
+           "kernels_dma_four.hip", "kernels_wide.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -60,12 +60,22 @@ nvfp4_status check_problem(const nvfp4_problem &p)
     return NVFP4_OK;
 }
 
+// A range of one problem's tiles on the wide 128 x 256 kernel, each tile's K
+// split into `split` slices.
+struct WideRange {
+    int prob;
+    int tile0, ntiles;
+    int split;
+};
+
 struct Plan {
     TileConfig cfg;
     int tile_m, tile_n, split_k;
     std::vector<int> prefix; // per input group, num_groups + 1 entries
     std::vector<int> order;  // launch order of the groups (longest K first)
+    std::vector<WideRange> ranges; // kWide128x256: the ranges, in launch order
     long long total_tiles;
+    long long workgroups;
     long long workspace_bytes;
 };
 
@@ -214,9 +224,93 @@ int small_m_split(long long total, int max_ktiles, int min_ktiles)
         {kTargetWorkgroups / total, (long long)std::max(1, max_ktiles / min_ktiles), (long long)kMaxSplitK});
 }
 
+// The wide 128 x 256 tile's contract: K % 256 == 0 and 16-byte aligned scales
+// in every non-empty group (A and B are 16-byte aligned in every valid call).
+bool wide_ok(const nvfp4_problem *problems, int num_groups)
+{
+    for (int g = 0; g < num_groups; ++g) {
+        const nvfp4_problem &p = problems[g];
+        if (empty_output(p))
+            continue;
+        if (p.K % 256 != 0 || ((((uintptr_t)p.SFA) | ((uintptr_t)p.SFB)) & 15) != 0)
+            return false;
+    }
+    return true;
+}
+
+// Wide-tile ranges of a launch (problems in plan->order, tiles counted in
+// plan->prefix), balanced over the chip's CUs.  The wide workgroup holds half
+// a CU (two run side by side), so the unit of balance is the CU.  Launches of
+// at least kWideNoSplitTiles tiles run whole tiles only (several rounds of
+// workgroups balance themselves).  Smaller ones run whole rounds of one tile
+// per CU, longest K first, and split the K of the remaining tiles so that
+// their work spreads over every CU: slices of about that remaining work / 256
+// CUs, at least one pair of K tiles (256 K) each and at most kWideMaxSplit per
+// tile.  A split whose partial tiles would take more than max_workspace
+// bytes is not made.
+constexpr int kCUs = 256;
+constexpr long long kWideNoSplitTiles = 4LL * kCUs;
+constexpr int kWideMaxSplit = 4;
+
+void plan_wide_ranges(const nvfp4_problem *problems, Plan *plan, long long max_workspace)
+{
+    plan->ranges.clear();
+    const long long T = plan->total_tiles;
+    auto tiles_of = [&](int g) { return plan->prefix[g + 1] - plan->prefix[g]; };
+    auto whole_only = [&]() {
+        plan->ranges.clear();
+        for (int g : plan->order)
+            if (tiles_of(g) > 0)
+                plan->ranges.push_back({g, 0, tiles_of(g), 1});
+    };
+    if (T >= kWideNoSplitTiles) {
+        whole_only();
+        return;
+    }
+    const long long n_whole = T / kCUs * kCUs;
+    // remaining work in 32-K sub-steps, and the slice length it asks for
+    long long left = n_whole, rem_work = 0;
+    for (int g : plan->order) {
+        const long long t = tiles_of(g);
+        const long long w = std::min(t, left);
+        left -= w;
+        rem_work += (t - w) * (problems[g].K / 32);
+    }
+    const long long L = std::max(1LL, (rem_work + kCUs - 1) / kCUs);
+    left = n_whole;
+    long long split_tiles = 0, slots = 0;
+    for (int g : plan->order) {
+        const int t = tiles_of(g);
+        if (t == 0)
+            continue;
+        const int w = (int)std::min<long long>(t, left);
+        left -= w;
+        if (w > 0)
+            plan->ranges.push_back({g, 0, w, 1});
+        if (w == t)
+            continue;
+        const long long k = problems[g].K / 32;
+        const int s = (int)std::max(1LL, std::min({(k + L - 1) / L, (long long)kWideMaxSplit, k / 8}));
+        plan->ranges.push_back({g, w, t - w, s});
+        if (s > 1) {
+            split_tiles += t - w;
+            slots += (long long)(t - w) * s;
+        }
+    }
+    const long long ws = slots > 0 ? nvfp4::kCounterBytes + slots * nvfp4::kWidePartialBytes : 0;
+    if (split_tiles > nvfp4::kMaxSplitTiles || ws > max_workspace)
+        whole_only();
+}
+
 // pow2: the power-of-two-scale path (one-wave 128 x 128 tiles on the scaled
 // FP4 MFMA, no K split), which needs K % 128 == 0 and 8-byte aligned scales.
-nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan, bool pow2 = false)
+// allow_wide: the wide 128 x 256 tile may be chosen (the blocked-scale path
+// turns it off, as it reads blocked scales on one-wave 128 x 128 tiles).
+// Largest workspace a plan may ask for (the wide tile's balancing split).
+constexpr long long kMaxPlanWorkspace = 256LL << 20;
+
+nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan, bool pow2 = false,
+                       bool allow_wide = true, long long max_workspace = kMaxPlanWorkspace)
 {
     if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS)
         return NVFP4_ERROR_INVALID_VALUE;
@@ -256,6 +350,7 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
             return problems[a].K > problems[b].K;
         });
         plan->workspace_bytes = 0;
+        plan->workgroups = total;
         return NVFP4_OK;
     }
     // Few 128 x 128 tiles: the 64-row kernels (eight waves per workgroup, two
@@ -288,7 +383,22 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
             plan->split_k = small_m_split(total, max_ktiles, 4);
         }
     } else {
+        // many tiles: the wide tile where its contract holds and it has at
+        // least one tile per CU (with fewer, the partial tiles of its
+        // balancing K split cost more than they save: measured 50 vs 31 us on
+        // 2048 x 2048 x 2048, 128 wide tiles, against four waves per 128 x 128
+        // tile), else one wave per 128 x 128 tile (or four, below)
         plan->cfg = nvfp4::kTile128x128;
+        if (allow_wide && wide_ok(problems, num_groups)) {
+            std::vector<int> prefix_w;
+            long long total_w = 0;
+            int kt_w = 0;
+            s = count_tiles(problems, num_groups, nvfp4::tile_shape(nvfp4::kWide128x256), &prefix_w, &total_w, &kt_w);
+            if (s != NVFP4_OK)
+                return s;
+            if (total_w >= kCUs)
+                plan->cfg = nvfp4::kWide128x256;
+        }
         s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
         if (s != NVFP4_OK)
             return s;
@@ -334,27 +444,94 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
             plan->cfg = nvfp4::kTile128x128K4;
     }
     plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
+    plan->workgroups = total * plan->split_k;
+    if (plan->cfg == nvfp4::kWide128x256) {
+        plan_wide_ranges(problems, plan, max_workspace);
+        long long slots = 0, wgs = 0;
+        int max_split = 1;
+        for (const WideRange &r : plan->ranges) {
+            wgs += (long long)r.ntiles * r.split;
+            if (r.split > 1)
+                slots += (long long)r.ntiles * r.split;
+            max_split = std::max(max_split, r.split);
+        }
+        plan->split_k = max_split;
+        plan->workgroups = wgs;
+        plan->workspace_bytes = slots > 0 ? nvfp4::kCounterBytes + slots * nvfp4::kWidePartialBytes : 0;
+    }
     return NVFP4_OK;
 }
 
 void fill_info(const Plan &plan, nvfp4_plan_info *info)
 {
     info->kernel = plan.total_tiles == 0 ? 0
+                   : plan.cfg == nvfp4::kWide128x256 ? 4
                    : plan.split_k > 1 ? 2
                    : plan.cfg == nvfp4::kTile128x128K4 ? 3 : 1;
     info->tile_m = plan.tile_m;
     info->tile_n = plan.tile_n;
     info->split_k = plan.split_k;
     info->total_tiles = (int)plan.total_tiles;
-    info->workgroups = (int)(plan.total_tiles * plan.split_k);
+    info->workgroups = (int)plan.workgroups;
     info->workspace_bytes = plan.workspace_bytes;
 }
 
 // Launches a finished plan with its workspace (plan.workspace_bytes at
 // `workspace`, counters zero): groups in plan order, kMaxGroupsPerLaunch per
 // launch.
+nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
+{
+    nvfp4::WideTable table;
+    memset(&table, 0, sizeof(table));
+    int n = 0, cnt = 0;
+    long long slot = 0;
+    auto flush = [&]() -> nvfp4_status {
+        if (n == 0)
+            return NVFP4_OK;
+        table.num_groups = n;
+        // launches of one call share the workspace: stream order keeps them apart
+        const hipError_t e = nvfp4::launch_wide(table, workspace, stream);
+        n = 0;
+        cnt = 0;
+        slot = 0;
+        return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
+    };
+    for (const WideRange &r : plan.ranges) {
+        const nvfp4_problem &p = problems[r.prob];
+        nvfp4::WideDesc &d = table.g[n];
+        d.A = (const uint8_t *)p.A;
+        d.SFA = (const uint8_t *)p.SFA;
+        d.B = (const uint8_t *)p.B;
+        d.SFB = (const uint8_t *)p.SFB;
+        d.C = (uint16_t *)p.C;
+        d.M = p.M;
+        d.N = p.N;
+        d.K = p.K;
+        d.tiles_m = (p.M + 127) / 128;
+        d.tiles_n = (p.N + 255) / 256;
+        d.tile0 = r.tile0;
+        d.split = r.split;
+        d.cnt0 = r.split > 1 ? cnt : 0;
+        d.slot0 = r.split > 1 ? (int)slot : 0;
+        if (r.split > 1) {
+            cnt += r.ntiles;
+            slot += (long long)r.ntiles * r.split;
+        }
+        table.prefix[n + 1] = table.prefix[n] + r.ntiles * r.split;
+        ++n;
+        if (n == nvfp4::kMaxWideRanges) {
+            const nvfp4_status s = flush();
+            if (s != NVFP4_OK)
+                return s;
+        }
+    }
+    return flush();
+}
+
 nvfp4_status launch_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
 {
+    if (plan.cfg == nvfp4::kWide128x256)
+        return launch_wide_plan(problems, plan, workspace, stream);
     nvfp4_status s = NVFP4_OK;
     GroupTable table;
     memset(&table, 0, sizeof(table));
@@ -459,7 +636,7 @@ nvfp4_status convert_one(const void *src, void *dst, int rows, int K, bool to_bl
 nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
 {
     Plan plan;
-    nvfp4_status s = make_plan(problems, num_groups, &plan);
+    nvfp4_status s = make_plan(problems, num_groups, &plan, false, false);
     if (s != NVFP4_OK)
         return s;
     for (int g = 0; g < num_groups; ++g) {
@@ -595,7 +772,7 @@ nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, c
     p.N = N;
     p.K = K;
     Plan plan;
-    nvfp4_status s = make_plan(&p, 1, &plan);
+    nvfp4_status s = make_plan(&p, 1, &plan, false, true, kScratchBytes);
     if (s != NVFP4_OK || plan.total_tiles == 0)
         return s;
     if (plan.workspace_bytes > kScratchBytes)

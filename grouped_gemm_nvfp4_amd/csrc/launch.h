@@ -76,6 +76,7 @@ enum TileConfig : int {
     kPanel64x64 = 3,    // 8 waves split K, each owning the 64 x 64 tile; K may be split
     kTile128x128Pow2 = 5, // one-wave 128 x 128 tiles on the scaled FP4 MFMA (power-of-two scales)
     kTile128x128Blocked = 6, // one-wave 128 x 128 direct-to-LDS tiles, scales in the blocked layout
+    kWide128x256 = 7,   // four waves share a 128 x 256 tile, decoded A exchanged through LDS
 };
 
 struct TileShape {
@@ -89,6 +90,8 @@ inline TileShape tile_shape(TileConfig c)
         return {64, 32, 256};
     case kPanel64x64:
         return {64, 64, 256};
+    case kWide128x256:
+        return {128, 256, 256};
     case kTile128x128K4:
     case kTile128x128Pow2:
     case kTile128x128Blocked:
@@ -129,6 +132,34 @@ hipError_t launch_tiled_dma(const GroupTable &table, TileConfig cfg, hipStream_t
 hipError_t launch_dma_one_wave(const GroupTable &table, bool pairs, hipStream_t stream);
 hipError_t launch_dma_special(const GroupTable &table, TileConfig cfg, hipStream_t stream);
 hipError_t launch_dma_four_wave(const GroupTable &table, bool pairs, hipStream_t stream);
+// The 128 x 256 wide tile (kernels_wide.hip).  A launch runs ranges of tiles:
+// tiles [tile0, tile0 + n) of one problem's grid, each tile's K split into
+// `split` slices (one workgroup each; 1 = whole K).  Slice j of the range's
+// tile i is workgroup prefix[g] + i * split + j.  With split > 1 every slice
+// stores its fp32 partial tile in partial slot slot0 + i * split + j of the
+// workspace and takes a ticket from counter cnt0 + i; the last adds the
+// slices in slice order and writes C.
+struct WideDesc {
+    const uint8_t *A, *SFA, *B, *SFB;
+    uint16_t *C;
+    int M, N, K;
+    int tiles_m, tiles_n; // ceil(M / 128), ceil(N / 256)
+    int tile0;            // first tile of the range (banded order of tile_order.h)
+    int split;            // K slices per tile
+    int cnt0, slot0;      // split > 1: first counter and first partial slot of the range
+};
+constexpr int kMaxWideRanges = 48;
+struct WideTable {
+    int num_groups; // ranges in this launch
+    int reserved;
+    int prefix[kMaxWideRanges + 1]; // workgroups before each range
+    WideDesc g[kMaxWideRanges];
+};
+static_assert(sizeof(WideTable) <= 4096, "kernel-argument budget");
+constexpr long long kWidePartialBytes = 128LL * 256 * 4; // one fp32 partial tile
+// Checks the contract (every K % 256 == 0; A, B, SFA, SFB 16-byte aligned;
+// the grid sizes; a workspace when some range splits) and launches.
+hipError_t launch_wide(const WideTable &table, void *workspace, hipStream_t stream);
 
 // Scale-layout conversion, batched: entry e moves the scales of a
 // rows[e] x (kb[e] = K/16) matrix between the plain [rows][K/16] layout and

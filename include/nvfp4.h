@@ -236,7 +236,10 @@ nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_g
  * memory on each GPU it runs on, until the process ends.  The call allocates
  * nothing (no hipMalloc, no library or torch allocation) and enqueues a small
  * kernel that clears the counters before the product, so it can be captured
- * on any stream.  Every call on a GPU shares that GPU's array: calls that
+ * on any stream.  One difference in planning: where nvfp4_gemm would split the
+ * K of some 128 x 256 tiles for balance and their partial tiles would not fit
+ * the array, this call keeps those tiles whole; C then differs from
+ * nvfp4_gemm's only by fp32 summation order, within the same accuracy bound.  Every call on a GPU shares that GPU's array: calls that
  * overlap in time on one GPU (other streams, concurrent graph replays) race
  * and give wrong results.  A plan whose workspace would exceed the array
  * returns NVFP4_ERROR_NOT_SUPPORTED (the planner keeps K-split launches at
@@ -250,12 +253,16 @@ nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, c
 typedef struct {
     int kernel;      /* 0: nothing to launch, 1: one tile per workgroup, 2: K split
                         across workgroups, 3: a 128 x 128 tile's K split across
-                        the workgroup's four waves */
+                        the workgroup's four waves, 4: four waves share a
+                        128 x 256 tile (decoded A exchanged through LDS); the
+                        tiles past whole rounds of one per CU may have their
+                        K split across workgroups for balance */
     int tile_m;      /* output rows per workgroup */
     int tile_n;      /* output columns per workgroup */
-    int split_k;     /* K slices per output tile (1 = none) */
+    int split_k;     /* K slices per output tile (1 = none; kernel 4: the
+                        largest split of any tile) */
     int total_tiles; /* output tiles over all groups */
-    int workgroups;  /* workgroups launched (total_tiles * split_k) */
+    int workgroups;  /* workgroups launched (kernels 1-3: total_tiles * split_k) */
     long long workspace_bytes; /* device workspace the call needs */
 } nvfp4_plan_info;
 

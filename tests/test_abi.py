@@ -114,7 +114,7 @@ def ceil_div(a, d):
 
 def test_plan_single():
     info = g.gemm_plan(8192, 8192, 8192)
-    assert info["kernel"] in (1, 2)
+    assert info["kernel"] == 4 and (info["tile_m"], info["tile_n"]) == (128, 256)
     tm, tn = info["tile_m"], info["tile_n"]
     assert info["total_tiles"] == ceil_div(8192, tm) * ceil_div(8192, tn)
     assert info["workgroups"] == info["total_tiles"] * info["split_k"]
@@ -144,7 +144,8 @@ def test_plan_group_prefix_is_exclusive_scan_of_tile_counts():
 ])
 def test_plan_tile_rows_follow_the_128_tile_count(M, N, K, tile_m):
     """Launches with M > 64 and at most 128 tiles of 128 x 128 take the 64-row
-    kernels; larger ones take 128 x 128 tiles."""
+    kernels; larger ones take 128-row tiles (128 x 256 wide tiles when every
+    K % 256 == 0, else 128 x 128)."""
     assert g.gemm_plan(M, N, K)["tile_m"] == tile_m
 
 
@@ -303,3 +304,52 @@ def test_k_limit_is_the_accuracy_bound():
         assert fn(ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 4, 4, K + 128, None) == b.NVFP4_ERROR_NOT_SUPPORTED
     # the worst-case accumulated error bound at the limit, as nvfp4.h states it
     assert K * 2.0 ** -27 + 2.0 ** -19 < 1e-3
+
+
+@pytest.mark.parametrize("M,N,K,kernel,tile_n", [
+    (8192, 8192, 8192, 4, 256),    # K % 256 == 0: the wide 128 x 256 tile
+    (2048, 1152, 4224, 3, 128),    # K % 256 != 0: 128 x 128 tiles (here four waves per tile)
+    (1024, 65536, 128, 1, 128),    # K % 256 != 0, many tiles: one wave per 128 x 128 tile
+])
+def test_plan_wide_tile_needs_k_multiple_of_256(M, N, K, kernel, tile_n):
+    info = g.gemm_plan(M, N, K)
+    assert (info["kernel"], info["tile_m"], info["tile_n"]) == (kernel, 128, tile_n)
+    assert info["total_tiles"] == ceil_div(M, 128) * ceil_div(N, tile_n)
+    assert info["split_k"] == 1 and info["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("M,N,K,workgroups,split", [
+    (8192, 8192, 8192, 2048, 1),   # 2048 tiles: several rounds of whole tiles
+    (4096, 3072, 7168, 512, 2),    # 384 tiles: 256 whole, the other 128 split in two
+    (2304, 4096, 1024, 384, 4),    # 288 tiles: 256 whole, the other 32 split in four
+    (8192, 2048, 256, 512, 1),     # K = 256: one pair of K tiles, nothing to split
+])
+def test_plan_wide_balance(M, N, K, workgroups, split):
+    """Wide launches of fewer than 1024 tiles run whole tiles in rounds of
+    one per CU and split the K of the rest over the CUs."""
+    info = g.gemm_plan(M, N, K)
+    assert info["kernel"] == 4
+    assert info["workgroups"] == workgroups and info["split_k"] == split
+    slots = workgroups - (info["total_tiles"] // 256 * 256) if split > 1 else 0
+    assert info["workspace_bytes"] == (16384 + slots * 128 * 256 * 4 if slots else 0)
+
+
+def test_plan_grouped_workloads_take_the_wide_tile():
+    """The 8-group MoE (304 tiles) and the 2-group workload (384 + 36 tiles):
+    one whole tile per CU, the rest split (the 2-group workload's short-K
+    group stays whole: its tiles are shorter than the slice length)."""
+    from grouped_gemm_nvfp4_amd import inputs
+    info, prefix = g.group_gemm_plan(inputs.workload_shapes(3)[1])
+    assert info["kernel"] == 4 and info["tile_n"] == 256 and prefix[-1] == info["total_tiles"] == 304
+    assert info["split_k"] == 4 and info["workgroups"] == 256 + 48 * 4
+    info, prefix = g.group_gemm_plan(inputs.workload_shapes(4)[1])
+    assert info["kernel"] == 4 and prefix[-1] == info["total_tiles"] == 420
+    assert info["split_k"] == 2 and info["workgroups"] == 256 + 128 * 2 + 36
+
+
+def test_plan_wide_tile_needs_a_tile_per_cu():
+    """Fewer than 256 wide tiles: the 128 x 128 route (here four waves per
+    tile), not the wide tile with its K split."""
+    info = g.gemm_plan(2048, 2048, 2048)
+    assert info["kernel"] == 3 and info["tile_n"] == 128
+    assert g.gemm_plan(4096, 2048, 2048)["kernel"] == 4  # 256 wide tiles

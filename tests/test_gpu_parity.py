@@ -874,3 +874,43 @@ def test_k_split_gemm_under_stream_capture(lib):
         graph.replay()
         torch.cuda.synchronize()
         assert_parity(bits(C), c16, bound, "K-split graph replay %d" % rep)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (4100, 2000, 256),   # ragged M and N, the shortest K (one pair of K tiles), 264 tiles
+    (2100, 4000, 512),   # 272 tiles: 256 whole, 16 split in two
+    (2537, 4100, 1280),  # odd number of K-tile pairs, 340 tiles, 84 split in three
+    (4096, 2048, 2048),  # 256 whole tiles
+    (2600, 2600, 1792),  # 231 wide tiles: the 128 x 128 route instead (few tiles)
+    (2304, 4096, 1024),  # 288 tiles: 256 whole, 32 split in four
+    (2200, 4096, 7168),  # 288 tiles, 32 split in four uneven slices (7, 7, 7, 7 of 28 pairs)
+])
+def test_wide_tile_shapes(lib, M, N, K):
+    """The 128 x 256 wide tile (four waves exchanging decoded A through LDS),
+    compared in full, with ragged edges, short and odd K-tile-pair counts, and
+    the balancing K split (partial tiles added by the last slice)."""
+    info = lib.gemm_plan(M, N, K)
+    wide = ((M + 127) // 128) * ((N + 255) // 256) >= 256
+    assert info["kernel"] == 4 if wide else info["kernel"] in (1, 3)
+    p = inputs.draw_problems(6200 + M + K, [(M, N, K)])[0]
+    check_full(lib, p, "wide %dx%dx%d" % (M, N, K))
+    assert np.array_equal(run_gemm(lib, p), run_gemm(lib, p)), "wide tile must be deterministic"
+
+
+def test_wide_tile_group_with_empty_and_zero_k(lib):
+    """A grouped wide launch: ragged groups, an empty group, a K = 0 group
+    (C is +0) and groups of different K."""
+    shapes = [(1700, 2300, 768), (0, 512, 256), (300, 2000, 0), (1025, 777, 256), (129, 3000, 1536),
+              (2000, 2570, 512)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["kernel"] == 4
+    probs = inputs.draw_problems(6300, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        if p.K == 0:
+            assert np.all(got == 0), "K = 0 group %d" % i
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "wide group %d" % i)

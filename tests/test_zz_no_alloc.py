@@ -105,3 +105,22 @@ def test_noalloc_captures_on_a_fresh_stream(lib):
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(_bits(C_na), _bits(C_ref)), "replay %d" % rep
+
+
+def test_noalloc_keeps_wide_tiles_whole_when_the_split_does_not_fit(lib):
+    """4096 x 3072 x 7168 (384 wide tiles): nvfp4_gemm splits the K of the 128
+    tiles past one round in two (32 MiB of partial tiles); the allocation-free
+    call keeps the tiles whole.  Both meet the oracle's parity rule."""
+    from grouped_gemm_nvfp4_amd import _binding as b
+    p = inputs.draw_problems(7103, [(4096, 3072, 7168)])[0]
+    info = lib.gemm_plan(p.M, p.N, p.K)
+    assert info["kernel"] == 4 and info["workspace_bytes"] > 16384 + 4194304
+    sh = torch.cuda.current_stream().cuda_stream
+    ops = _operands(p)
+    C_ref, C_na = _poisoned(p.M, p.N), _poisoned(p.M, p.N)
+    assert _call(b.raw_gemm, ops, C_ref, p, sh) == b.NVFP4_OK
+    assert _call(b.raw_gemm_noalloc, ops, C_na, p, sh) == b.NVFP4_OK
+    torch.cuda.synchronize()
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+    assert_parity(_bits(C_ref), c16, bound, "gemm 4096x3072x7168")
+    assert_parity(_bits(C_na), c16, bound, "noalloc 4096x3072x7168")
