@@ -250,7 +250,10 @@ bool wide_ok(const nvfp4_problem *problems, int num_groups)
 // bytes is not made.
 constexpr int kCUs = 256;
 constexpr long long kWideNoSplitTiles = 4LL * kCUs;
-constexpr int kWideMaxSplit = 4;
+constexpr int kWideMaxSplit = nvfp4::kMaxWideSplit;
+// The 64 x 128 small-M tile (one workgroup per CU) is taken with at least this
+// many tiles.
+constexpr long long kSkinnyMinTiles = 192;
 
 void plan_wide_ranges(const nvfp4_problem *problems, Plan *plan, long long max_workspace)
 {
@@ -367,7 +370,33 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
             return s;
         few_tiles = total128 <= kPanelMaxTiles128;
     }
-    if (max_m > 0 && (max_m <= 64 || few_tiles)) {
+    // 32 < M <= 64 in every group, every K % 256 == 0 and aligned scales, and
+    // enough columns for one 64 x 128 tile per CU without a K split: the tile
+    // whose two column waves share their decoded A rows (kernels_wide.hip).
+    // Measured, event means: 64 x 28672 x 4096 29.2 vs 32.7 us on the panel
+    // kernel.  With a K split its 32 KiB partial tiles cost more than the panel
+    // kernel's 16 KiB ones save (64 x 7168 x 16384, four slices: 35 vs 28 us),
+    // so smaller launches stay on the 64-row kernels.
+    bool skinny = false;
+    if (max_m > 32 && max_m <= 64 && allow_wide && wide_ok(problems, num_groups)) {
+        std::vector<int> prefix_s;
+        long long total_s = 0;
+        int kt_s = 0;
+        s = count_tiles(problems, num_groups, nvfp4::tile_shape(nvfp4::kSkinny64x128), &prefix_s, &total_s, &kt_s);
+        if (s != NVFP4_OK)
+            return s;
+        if (total_s >= kSkinnyMinTiles) {
+            skinny = true;
+            plan->cfg = nvfp4::kSkinny64x128;
+            plan->split_k = 1;
+            plan->prefix = prefix_s;
+            total = total_s;
+            max_ktiles = kt_s;
+        }
+    }
+    if (skinny) {
+        // (the ranges are set below)
+    } else if (max_m > 0 && (max_m <= 64 || few_tiles)) {
         // panel: each wave takes at least one 256-K tile of a slice (8 waves)
         plan->cfg = nvfp4::kPanel64x64;
         s = count_tiles(problems, num_groups, nvfp4::tile_shape(plan->cfg), &plan->prefix, &total, &max_ktiles);
@@ -445,6 +474,17 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     }
     plan->workspace_bytes = nvfp4::workspace_bytes(plan->cfg, total, plan->split_k);
     plan->workgroups = total * plan->split_k;
+    if (plan->cfg == nvfp4::kSkinny64x128) {
+        // one range per problem, whole tiles
+        plan->ranges.clear();
+        for (int g : plan->order) {
+            const int t = plan->prefix[g + 1] - plan->prefix[g];
+            if (t > 0)
+                plan->ranges.push_back({g, 0, t, 1});
+        }
+        plan->workgroups = total;
+        plan->workspace_bytes = 0;
+    }
     if (plan->cfg == nvfp4::kWide128x256) {
         plan_wide_ranges(problems, plan, max_workspace);
         long long slots = 0, wgs = 0;
@@ -466,6 +506,7 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
 {
     info->kernel = plan.total_tiles == 0 ? 0
                    : plan.cfg == nvfp4::kWide128x256 ? 4
+                   : plan.cfg == nvfp4::kSkinny64x128 ? 5
                    : plan.split_k > 1 ? 2
                    : plan.cfg == nvfp4::kTile128x128K4 ? 3 : 1;
     info->tile_m = plan.tile_m;
@@ -481,14 +522,20 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
 // launch.
 nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
 {
+    const nvfp4::TileShape ts = nvfp4::tile_shape(plan.cfg);
+    const int bm = ts.tile_m, bn = ts.tile_n;
     nvfp4::WideTable table;
     memset(&table, 0, sizeof(table));
+    table.tile_rows = bm;
+    table.tile_cols = bn;
     int n = 0, cnt = 0;
     long long slot = 0;
     auto flush = [&]() -> nvfp4_status {
         if (n == 0)
             return NVFP4_OK;
         table.num_groups = n;
+        table.tile_rows = bm;
+        table.tile_cols = bn;
         // launches of one call share the workspace: stream order keeps them apart
         const hipError_t e = nvfp4::launch_wide(table, workspace, stream);
         n = 0;
@@ -507,8 +554,8 @@ nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, v
         d.M = p.M;
         d.N = p.N;
         d.K = p.K;
-        d.tiles_m = (p.M + 127) / 128;
-        d.tiles_n = (p.N + 255) / 256;
+        d.tiles_m = (p.M + bm - 1) / bm;
+        d.tiles_n = (p.N + bn - 1) / bn;
         d.tile0 = r.tile0;
         d.split = r.split;
         d.cnt0 = r.split > 1 ? cnt : 0;
@@ -530,7 +577,7 @@ nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, v
 
 nvfp4_status launch_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
 {
-    if (plan.cfg == nvfp4::kWide128x256)
+    if (plan.cfg == nvfp4::kWide128x256 || plan.cfg == nvfp4::kSkinny64x128)
         return launch_wide_plan(problems, plan, workspace, stream);
     nvfp4_status s = NVFP4_OK;
     GroupTable table;
@@ -719,7 +766,7 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
 // process ends.  Host code never uses the array's name as an address: the
 // device address comes from hipGetSymbolAddress, taken once per device (with
 // that device current) on the entry point's first call there.
-constexpr long long kScratchBytes = nvfp4::kCounterBytes + 4LL * 1024 * 1024;
+constexpr long long kScratchBytes = nvfp4::kCounterBytes + 8LL * 1024 * 1024;
 static_assert(kScratchBytes == NVFP4_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 

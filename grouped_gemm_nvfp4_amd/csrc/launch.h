@@ -77,6 +77,7 @@ enum TileConfig : int {
     kTile128x128Pow2 = 5, // one-wave 128 x 128 tiles on the scaled FP4 MFMA (power-of-two scales)
     kTile128x128Blocked = 6, // one-wave 128 x 128 direct-to-LDS tiles, scales in the blocked layout
     kWide128x256 = 7,   // four waves share a 128 x 256 tile, decoded A exchanged through LDS
+    kSkinny64x128 = 8,  // eight waves (4 K-groups of 2) share a 64 x 128 tile, decoded A exchanged
 };
 
 struct TileShape {
@@ -92,6 +93,8 @@ inline TileShape tile_shape(TileConfig c)
         return {64, 64, 256};
     case kWide128x256:
         return {128, 256, 256};
+    case kSkinny64x128:
+        return {64, 128, 256};
     case kTile128x128K4:
     case kTile128x128Pow2:
     case kTile128x128Blocked:
@@ -149,14 +152,20 @@ struct WideDesc {
     int cnt0, slot0;      // split > 1: first counter and first partial slot of the range
 };
 constexpr int kMaxWideRanges = 48;
+// Largest K split of a 128 x 256 tile (the kernel adds at most this many slices).
+constexpr int kMaxWideSplit = 4;
 struct WideTable {
     int num_groups; // ranges in this launch
+    int tile_rows;  // 128 (the wide tile) or 64 (the small-M tile)
+    int tile_cols;  // 256 or 128
     int reserved;
     int prefix[kMaxWideRanges + 1]; // workgroups before each range
     WideDesc g[kMaxWideRanges];
 };
 static_assert(sizeof(WideTable) <= 4096, "kernel-argument budget");
-constexpr long long kWidePartialBytes = 128LL * 256 * 4; // one fp32 partial tile
+// one fp32 partial tile of a 128 x 256 and of a 64 x 128 tile
+constexpr long long kWidePartialBytes = 128LL * 256 * 4;
+constexpr long long kSkinnyPartialBytes = 64LL * 128 * 4;
 // Checks the contract (every K % 256 == 0; A, B, SFA, SFB 16-byte aligned;
 // the grid sizes; a workspace when some range splits) and launches.
 hipError_t launch_wide(const WideTable &table, void *workspace, hipStream_t stream);

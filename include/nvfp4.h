@@ -242,9 +242,10 @@ nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_g
  * nvfp4_gemm's only by fp32 summation order, within the same accuracy bound.  Every call on a GPU shares that GPU's array: calls that
  * overlap in time on one GPU (other streams, concurrent graph replays) race
  * and give wrong results.  A plan whose workspace would exceed the array
- * returns NVFP4_ERROR_NOT_SUPPORTED (the planner keeps K-split launches at
- * 256 workgroups of at most 16 KiB of partial sums, within it). */
-#define NVFP4_NOALLOC_SCRATCH_BYTES (16384 + 4194304)
+ * returns NVFP4_ERROR_NOT_SUPPORTED (the planner keeps the K-split launches
+ * of small products at 256 workgroups of at most 32 KiB of partial sums,
+ * within it). */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (16384 + 8388608)
 nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, const void *SFB,
                                 void *C, int M, int N, int K, hipStream_t stream);
 
@@ -256,7 +257,9 @@ typedef struct {
                         the workgroup's four waves, 4: four waves share a
                         128 x 256 tile (decoded A exchanged through LDS); the
                         tiles past whole rounds of one per CU may have their
-                        K split across workgroups for balance */
+                        K split across workgroups for balance; 5: eight waves
+                        share a 64 x 128 tile (32 < M <= 64, at least 192
+                        tiles) */
     int tile_m;      /* output rows per workgroup */
     int tile_n;      /* output columns per workgroup */
     int split_k;     /* K slices per output tile (1 = none; kernel 4: the

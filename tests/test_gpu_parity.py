@@ -189,19 +189,38 @@ def test_four_wave_direct_tiles(lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,split", [
-    (64, 6144, 8192, 2),    # scale groups of four K tiles, K split in two
-    (64, 16384, 4096, 1),   # no split
     (48, 12288, 4128, 1),   # K % 256 != 0: byte scale loads, ragged last K tile
     (64, 6400, 8224, 2),    # byte scale loads with a K split
-    (33, 7000, 8192, 2),    # ragged M and N
+    (63, 7000, 4640, 2),    # ragged M and N, K % 256 != 0
 ])
 def test_panel_shapes(lib, M, N, K, split):
-    """M <= 64 with enough 64 x 64 tiles (and K slices) to fill the chip takes
-    the panel kernel."""
+    """M <= 64 with enough 64 x 64 tiles (and K slices) to fill the chip, and
+    K % 256 != 0 (outside the 64 x 128 tile's contract), takes the panel
+    kernel."""
     info = lib.gemm_plan(M, N, K)
     assert info["tile_n"] == 64 and info["split_k"] == split
     p = inputs.draw_problems(5000 + M + K, [(M, N, K)])[0]
     check_full(lib, p, "panel %dx%dx%d split %d" % (M, N, K, split))
+
+
+@pytest.mark.parametrize("M,N,K,tile_n,split", [
+    (64, 28672, 4096, 128, 1),  # 224 tiles of 64 x 128: two column waves share decoded A
+    (40, 24576, 2048, 128, 1),  # 192 tiles, ragged M, one pair of K tiles per K-group
+    (33, 30000, 1280, 128, 1),  # ragged M and N, 5 pairs: K-groups of 2, 2, 1 and 0 pairs
+    (64, 6144, 8192, 64, 2),    # too few 64 x 128 tiles: the panel kernel
+])
+def test_small_m_wide_tile_shapes(lib, M, N, K, tile_n, split):
+    """32 < M <= 64 with every K % 256 == 0 and at least 192 tiles of 64 x 128
+    takes the 64 x 128 tile of the direct-to-LDS pipeline (four K-groups of two
+    waves sharing their decoded A rows); with fewer, the panel kernel."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == (5 if tile_n == 128 else 2) and (info["tile_m"], info["tile_n"]) == (64, tile_n)
+    assert info["split_k"] == split
+    p = inputs.draw_problems(5400 + M + K, [(M, N, K)])[0]
+    got = run_gemm(lib, p)
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(got, c16, bound, "small-M wide %dx%dx%d split %d" % (M, N, K, split))
+    assert np.array_equal(got, run_gemm(lib, p)), "the K-group and slice sums must not depend on timing"
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 6144, 8192), (40, 500, 1024), (200, 136, 512)])
@@ -442,8 +461,8 @@ def test_group_panel_one_row_block(lib):
 
 def test_group_small_m_panel(lib):
     """Small-M groups whose 64 x 64 tiles fill the chip take the panel kernel
-    with a K split; ragged N and M in some groups."""
-    shapes = [(64, 2048, 8192), (17, 2000, 8192), (64, 2048, 4096), (50, 1900, 8192)]
+    with a K split (one K % 256 != 0); ragged N and M in some groups."""
+    shapes = [(64, 2048, 8192), (17, 2000, 8192), (64, 2048, 4128), (50, 1900, 8192)]
     info, _ = lib.group_gemm_plan(shapes)
     assert info["tile_n"] == 64 and info["split_k"] > 1
     probs = inputs.draw_problems(38, shapes)
@@ -914,3 +933,22 @@ def test_wide_tile_group_with_empty_and_zero_k(lib):
             continue
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "wide group %d" % i)
+
+
+def test_group_small_m_wide_tile(lib):
+    """A grouped launch on the 64 x 128 small-M tile: ragged groups, a K = 0
+    group (zero C), an empty group, different K."""
+    shapes = [(64, 8192, 2048), (40, 8192, 4096), (50, 8000, 1024), (64, 300, 0), (0, 128, 256),
+              (64, 320, 2048)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert info["kernel"] == 5 and info["split_k"] == 1
+    probs = inputs.draw_problems(40, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        if p.K == 0:
+            assert np.all(got == 0)
+            continue
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+        assert_parity(got, c16, bound, "small-M wide group %d" % i)

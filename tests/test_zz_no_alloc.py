@@ -55,7 +55,7 @@ def test_noalloc_equals_gemm_on_consecutive_calls(lib):
     sh = torch.cuda.current_stream().cuda_stream
     for p in probs:
         info = lib.gemm_plan(p.M, p.N, p.K)
-        assert info["split_k"] > 1 and 0 < info["workspace_bytes"] <= 16384 + 4194304
+        assert info["split_k"] > 1 and 0 < info["workspace_bytes"] <= 16384 + 8388608
         ops = _operands(p)
         C_ref, C_na = _poisoned(p.M, p.N), _poisoned(p.M, p.N)
         assert _call(b.raw_gemm, ops, C_ref, p, sh) == b.NVFP4_OK
@@ -114,7 +114,7 @@ def test_noalloc_keeps_wide_tiles_whole_when_the_split_does_not_fit(lib):
     from grouped_gemm_nvfp4_amd import _binding as b
     p = inputs.draw_problems(7103, [(4096, 3072, 7168)])[0]
     info = lib.gemm_plan(p.M, p.N, p.K)
-    assert info["kernel"] == 4 and info["workspace_bytes"] > 16384 + 4194304
+    assert info["kernel"] == 4 and info["workspace_bytes"] > 16384 + 8388608
     sh = torch.cuda.current_stream().cuda_stream
     ops = _operands(p)
     C_ref, C_na = _poisoned(p.M, p.N), _poisoned(p.M, p.N)
