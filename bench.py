@@ -22,8 +22,8 @@ number of steps), and the CPU oracle's throughput on a bounded sample of the
 headline workload.  The roofline's "traffic" (HBM bytes per launch from the
 FETCH_SIZE and WRITE_SIZE counters) comes from profiles/hbm_traffic.txt and is
 reported only while the kernel sources it was measured on are unchanged.  The
-GPU's graphics clock is sampled (amdsmi) while the headline workload runs
-back to back.
+GPU's graphics clock (the driver's DPM table in sysfs) is sampled while the
+headline workload runs back to back.
 
     python bench.py --copy-probe BYTES
 
@@ -226,52 +226,58 @@ def rocm_version():
         return None
 
 
-def sample_gfx_clock(run_step, seconds):
-    """Graphics clock (MHz, amdsmi) sampled every 10 ms from a helper thread
-    while the calling thread issues run_step() back to back for `seconds`.
-    Returns a summary dict, or one with an "error" when amdsmi is unusable."""
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-    except Exception as e:  # noqa: BLE001 - reporting only
-        return {"error": "amdsmi unavailable: %s" % (e,)}
-    samples, stop = [], threading.Event()
-    try:
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
-
-        def sampler():
-            while not stop.is_set():
-                try:
-                    info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
-                    samples.append(float(info["clk"]))
-                except Exception:  # noqa: BLE001
-                    pass
-                stop.wait(0.01)
-
-        th = threading.Thread(target=sampler, daemon=True)
-        th.start()
-        t0 = time.perf_counter()
-        i = 0
-        while time.perf_counter() - t0 < seconds:
-            run_step(i)
-            i += 1
-            if i % 64 == 0:
-                import torch
-                torch.cuda.synchronize()
-        import torch
-        torch.cuda.synchronize()
-        stop.set()
-        th.join()
-    finally:
+def read_sclk_mhz():
+    """The current graphics clock (MHz) from the driver's DPM table in sysfs
+    (the entry marked '*' of pp_dpm_sclk), or None."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:  # noqa: BLE001
-            pass
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        if m:
+                            return float(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def sample_gfx_clock(run_step, seconds):
+    """Graphics clock (MHz, the driver's sysfs DPM table) sampled every 10 ms
+    from a helper thread while the calling thread issues run_step() back to
+    back for `seconds`.  Returns a summary dict, or one with an "error" when no
+    clock can be read."""
+    if read_sclk_mhz() is None:
+        return {"error": "no readable pp_dpm_sclk"}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            stop.wait(0.01)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        run_step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
     if not samples:
         return {"error": "no clock samples"}
     # the first samples can predate the load: report the busy part
     busy = samples[len(samples) // 5:] or samples
-    return {"window_s": seconds, "samples": len(samples),
+    return {"source": "pp_dpm_sclk", "window_s": seconds, "samples": len(samples),
             "median_mhz": float(np.median(busy)), "min_mhz": float(np.min(busy)),
             "max_mhz": float(np.max(busy))}
 

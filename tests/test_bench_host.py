@@ -118,10 +118,22 @@ def test_output_line_carries_every_field():
 
 
 def test_clock_sampler_reports_without_a_gpu():
-    """Without a usable GPU the clock sampler returns an error record instead
+    """Without a readable clock the sampler returns an error record instead
     of raising (the bench line still prints)."""
-    r = bench.sample_gfx_clock(lambda i: None, 0.01)
-    assert isinstance(r, dict) and ("error" in r or "median_mhz" in r)
+    if bench.read_sclk_mhz() is None:
+        r = bench.sample_gfx_clock(lambda i: None, 0.01)
+        assert r == {"error": "no readable pp_dpm_sclk"}
+
+
+def test_sclk_parsing(tmp_path, monkeypatch):
+    """The clock is the DPM entry marked with '*'."""
+    import glob as glob_mod
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1698Mhz *\n2: 2400Mhz\n")
+    monkeypatch.setattr(glob_mod, "glob", lambda pattern: [str(f)])
+    assert bench.read_sclk_mhz() == 1698.0
+    f.write_text("S: 94Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz() == 94.0
 
 
 def test_metadata_helpers():
