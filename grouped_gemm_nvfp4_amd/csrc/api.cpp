@@ -520,7 +520,9 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
 // Launches a finished plan with its workspace (plan.workspace_bytes at
 // `workspace`, counters zero): groups in plan order, kMaxGroupsPerLaunch per
 // launch.
-nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
+// blocked: SFA and SFB of every problem are in the blocked layout
+nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream,
+                              bool blocked = false)
 {
     const nvfp4::TileShape ts = nvfp4::tile_shape(plan.cfg);
     const int bm = ts.tile_m, bn = ts.tile_n;
@@ -528,6 +530,7 @@ nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, v
     memset(&table, 0, sizeof(table));
     table.tile_rows = bm;
     table.tile_cols = bn;
+    table.blocked = blocked ? 1 : 0;
     int n = 0, cnt = 0;
     long long slot = 0;
     auto flush = [&]() -> nvfp4_status {
@@ -536,6 +539,7 @@ nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, v
         table.num_groups = n;
         table.tile_rows = bm;
         table.tile_cols = bn;
+        table.blocked = blocked ? 1 : 0;
         // launches of one call share the workspace: stream order keeps them apart
         const hipError_t e = nvfp4::launch_wide(table, workspace, stream);
         n = 0;
@@ -683,7 +687,7 @@ nvfp4_status convert_one(const void *src, void *dst, int rows, int K, bool to_bl
 nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
 {
     Plan plan;
-    nvfp4_status s = make_plan(problems, num_groups, &plan, false, false);
+    nvfp4_status s = make_plan(problems, num_groups, &plan);
     if (s != NVFP4_OK)
         return s;
     for (int g = 0; g < num_groups; ++g) {
@@ -693,6 +697,14 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
     }
     if (plan.total_tiles == 0)
         return NVFP4_OK;
+    if (plan.cfg == nvfp4::kWide128x256 || plan.cfg == nvfp4::kSkinny64x128) {
+        // the shared-decode tiles read the blocked scales directly
+        void *workspace = nullptr;
+        s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
+        if (s != NVFP4_OK)
+            return s;
+        return launch_wide_plan(problems, plan, workspace, stream, true);
+    }
     bool direct = plan.cfg == nvfp4::kTile128x128;
     for (int g = 0; g < num_groups; ++g)
         if (!empty_output(problems[g]) && problems[g].K % 128 != 0)

@@ -79,7 +79,10 @@ struct Shape {
     static constexpr int kBOff = kARows * kRowBytes;                   // in a stage
     static constexpr int kStageBytes = (kARows + kBRows) * kRowBytes;
     static constexpr int kWaveBytes = 2 * kStageBytes + 2 * kPairBytes;
-    static constexpr int kLoadsOdd = 2 * RA + 4, kLoadsEven = 2 * RA + 6; // load instructions per K tile
+    // load instructions per K tile: data 2 RA + 4; on even tiles the scale
+    // pair, 2 plain 16-byte loads or 2 RA + 4 blocked 4-byte loads
+    static constexpr int kLoadsOdd = 2 * RA + 4;
+    static constexpr int kLoadsEvenPlain = kLoadsOdd + 2, kLoadsEvenBlocked = kLoadsOdd + 2 * RA + 4;
     static constexpr int kXBuf = RB * kXWave;                          // one exchange buffer of a K-group
     static constexpr int kXOff = kWaves * kWaveBytes;                  // exchange buffers [K-group][2]
     static constexpr int kLdsBytes = kXOff + (CW > 1 ? KG * 2 * kXBuf : 0);
@@ -115,14 +118,21 @@ typedef __attribute__((address_space(3))) void wide_lds_void;
         asm volatile("" ::: "memory");                                                                               \
     } while (0)
 
-template <int RB, int CW, int KG>
+// kBlocked: SFA and SFB in the blocked layout of nvfp4.h (512-byte atoms of
+// 128 rows x 4 scale blocks, a 128-row tile's atoms in K order; row r, block c
+// of an atom at (r % 32) * 16 + (r / 32) * 4 + c).  A row's four blocks of a
+// 64-K group are then one dword of its atom: the wave fetches exactly its
+// rows' dwords of the pair's four atoms (4-byte direct loads, [atom][row] in
+// the pair buffer) instead of 16 contiguous bytes per row.
+template <int RB, int CW, int KG, bool kBlocked>
 __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *ws)
 {
     using namespace wide;
     using Sh = Shape<RB, CW, KG>;
     constexpr int BM = Sh::BM, BN = Sh::BN, kThreads = Sh::kThreads, RA = Sh::RA;
     constexpr int kARows = Sh::kARows, kBOff = Sh::kBOff, kStageBytes = Sh::kStageBytes;
-    constexpr int kWaveBytes = Sh::kWaveBytes, kLoadsOdd = Sh::kLoadsOdd, kLoadsEven = Sh::kLoadsEven;
+    constexpr int kWaveBytes = Sh::kWaveBytes, kLoadsOdd = Sh::kLoadsOdd;
+    constexpr int kLoadsEven = kBlocked ? Sh::kLoadsEvenBlocked : Sh::kLoadsEvenPlain;
     __shared__ __attribute__((aligned(16))) uint8_t lds[Sh::kLdsBytes];
 
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -157,8 +167,18 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
     const int a_rows = max(0, min(kARows, M - arow)), b_rows = max(0, min(kBRows, N - brow));
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)arow * kb_row, (uint64_t)a_rows * kb_row);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)brow * kb_row, (uint64_t)b_rows * kb_row);
-    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)arow * ks_row, (uint64_t)a_rows * ks_row);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)brow * ks_row, (uint64_t)b_rows * ks_row);
+    // blocked scales: the 128-row tiles holding this wave's rows (whole tiles
+    // of atoms; rows past M or N are the layout's zero padding) and the row
+    // block of its first A and B row within them
+    const int rest_k = K / 64;
+    const int atile = arow / 128, btile = brow / 128;
+    const int rba = (arow % 128) / 32, rbb = (brow % 128) / 32;
+    const __amdgpu_buffer_rsrc_t rSA =
+        kBlocked ? make_rsrc(d.SFA + (long)atile * rest_k * 512, atile < (M + 127) / 128 ? (uint64_t)rest_k * 512 : 0)
+                 : make_rsrc(d.SFA + (long)arow * ks_row, (uint64_t)a_rows * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB =
+        kBlocked ? make_rsrc(d.SFB + (long)btile * rest_k * 512, btile < (N + 127) / 128 ? (uint64_t)rest_k * 512 : 0)
+                 : make_rsrc(d.SFB + (long)brow * ks_row, (uint64_t)b_rows * ks_row);
 
     uint8_t *const region = lds + wv * kWaveBytes;
     uint8_t *const xbase = lds + Sh::kXOff + kg * 2 * Sh::kXBuf; // this K-group's exchange buffers
@@ -187,11 +207,30 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
                                                      0, 0, 0);
         if (pair) {
             uint8_t *pb = region + 2 * kStageBytes + ((kt >> 1) & 1) * kPairBytes;
-            const uint32_t ks = (uint32_t)kt * 8;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (wide_lds_void *)(pb + kPairA), 16,
-                                                     live && lane < kARows ? pa_off + ks : kOutOfRange, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (wide_lds_void *)(pb + kPairB), 16,
-                                                     live ? pa_off + ks : kOutOfRange, 0, 0, 0);
+            if constexpr (kBlocked) {
+                // dword idx = 64 q + lane of the pair buffer: atom j = idx / rows,
+                // row r = idx % rows; the pair's atoms are 2 kt .. 2 kt + 3
+#pragma unroll
+                for (int q = 0; q < 2 * RA; ++q) {
+                    const int idx = 64 * q + lane, j = idx / kARows, r = idx % kARows;
+                    const uint32_t off = (uint32_t)((2 * kt + j) * 512 + (r % 32) * 16 + (rba + r / 32) * 4);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (wide_lds_void *)(pb + kPairA + 256 * q), 4,
+                                                             live ? off : kOutOfRange, 0, 0, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int idx = 64 * q + lane, j = idx / kBRows, r = idx % kBRows;
+                    const uint32_t off = (uint32_t)((2 * kt + j) * 512 + (r % 32) * 16 + (rbb + r / 32) * 4);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (wide_lds_void *)(pb + kPairB + 256 * q), 4,
+                                                             live ? off : kOutOfRange, 0, 0, 0);
+                }
+            } else {
+                const uint32_t ks = (uint32_t)kt * 8;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (wide_lds_void *)(pb + kPairA), 16,
+                                                         live && lane < kARows ? pa_off + ks : kOutOfRange, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (wide_lds_void *)(pb + kPairB), 16,
+                                                         live ? pa_off + ks : kOutOfRange, 0, 0, 0);
+            }
         }
     };
 
@@ -202,16 +241,29 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
     uint32_t wa[RA], wb0, wb1;
     auto read_raw = [&](int kt, int g) {
         const uint8_t *sb = region + (kt & 1) * kStageBytes;
-        const uint8_t *pb = region + 2 * kStageBytes + ((kt >> 1) & 1) * kPairBytes + 8 * (kt & 1) + 4 * g;
+        const uint8_t *pq = region + 2 * kStageBytes + ((kt >> 1) & 1) * kPairBytes;
+        // the scale dword of a row for 64-K group g of tile kt
+        auto scale_a = [&](int row) -> uint32_t {
+            if constexpr (kBlocked)
+                return *(const uint32_t *)(pq + kPairA + ((2 * (kt & 1) + g) * kARows + row) * 4);
+            else
+                return *(const uint32_t *)(pq + kPairA + 16 * row + 8 * (kt & 1) + 4 * g);
+        };
+        auto scale_b = [&](int row) -> uint32_t {
+            if constexpr (kBlocked)
+                return *(const uint32_t *)(pq + kPairB + ((2 * (kt & 1) + g) * kBRows + row) * 4);
+            else
+                return *(const uint32_t *)(pq + kPairB + 16 * row + 8 * (kt & 1) + 4 * g);
+        };
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
             ra[r] = *(const u32x4 *)(sb + kAOff + tiled::swz(32 * r + l32, 2 * g + h));
-            wa[r] = *(const uint32_t *)(pb + kPairA + 16 * (32 * r + l32)) >> sh;
+            wa[r] = scale_a(32 * r + l32) >> sh;
         }
         rb0 = *(const u32x4 *)(sb + kBOff + tiled::swz(l32, 2 * g + h));
         rb1 = *(const u32x4 *)(sb + kBOff + tiled::swz(32 + l32, 2 * g + h));
-        wb0 = *(const uint32_t *)(pb + kPairB + 16 * l32) >> sh;
-        wb1 = *(const uint32_t *)(pb + kPairB + 16 * (32 + l32)) >> sh;
+        wb0 = scale_b(l32) >> sh;
+        wb1 = scale_b(32 + l32) >> sh;
     };
 
     // fragments of the current sub-step (A_cur: this wave's row blocks) and of
@@ -551,15 +603,17 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
 }
 
 // 128 x 256 wide tiles: four waves, two workgroups per CU
+template <bool kBlocked>
 __global__ __launch_bounds__(256, 2) void gemm_wide_kernel(WideTable tab, uint8_t *ws)
 {
-    wide_tile<4, 4, 1>(tab, (int)blockIdx.x, ws);
+    wide_tile<4, 4, 1, kBlocked>(tab, (int)blockIdx.x, ws);
 }
 
 // 64 x 128 small-M tiles: eight waves (four K-groups of two), one workgroup per CU
+template <bool kBlocked>
 __global__ __launch_bounds__(512, 1) void gemm_skinny_kernel(WideTable tab, uint8_t *ws)
 {
-    wide_tile<2, 2, 4>(tab, (int)blockIdx.x, ws);
+    wide_tile<2, 2, 4, kBlocked>(tab, (int)blockIdx.x, ws);
 }
 
 } // namespace
@@ -588,7 +642,11 @@ hipError_t launch_wide(const WideTable &table, void *workspace, hipStream_t stre
     }
     uint8_t *ws = (uint8_t *)workspace;
     void *args[] = {const_cast<WideTable *>(&table), &ws};
-    const void *fn = skinny ? (const void *)gemm_skinny_kernel : (const void *)gemm_wide_kernel;
+    if (table.blocked != 0 && table.blocked != 1)
+        return hipErrorInvalidValue;
+    const bool blocked = table.blocked == 1;
+    const void *fn = skinny ? (blocked ? (const void *)gemm_skinny_kernel<true> : (const void *)gemm_skinny_kernel<false>)
+                            : (blocked ? (const void *)gemm_wide_kernel<true> : (const void *)gemm_wide_kernel<false>);
     return hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(skinny ? 512 : 256), args, 0, stream);
 }
 

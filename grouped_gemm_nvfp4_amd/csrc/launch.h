@@ -158,7 +158,7 @@ struct WideTable {
     int num_groups; // ranges in this launch
     int tile_rows;  // 128 (the wide tile) or 64 (the small-M tile)
     int tile_cols;  // 256 or 128
-    int reserved;
+    int blocked;    // 1: SFA and SFB in the blocked layout (512-byte atoms), 0: [rows][K/16]
     int prefix[kMaxWideRanges + 1]; // workgroups before each range
     WideDesc g[kMaxWideRanges];
 };

@@ -190,14 +190,15 @@ nvfp4_status nvfp4_scales_from_blocked(const void *blocked, void *sf, int rows, 
 
 /* nvfp4_gemm / nvfp4_group_gemm with SFA and SFB in the blocked layout
  * (16-byte aligned, nvfp4_blocked_scale_bytes(M or N, K) bytes each).  Where
- * the plain call would run one-wave 128 x 128 tiles and every K is a multiple
- * of 128 (large and grouped products), that kernel reads the blocked scales
- * directly.  Otherwise the scales are first converted to the plain layout
- * inside the library's per-stream device workspace (so the call may allocate
- * it, and returns NOT_SUPPORTED inside a stream capture if it would have to)
- * and the plain path runs.  Either way C is bitwise what nvfp4_gemm gives for
- * the same scales.  Other arguments, limits and errors as for the plain entry
- * points. */
+ * the plain call would run the shared-decode 128 x 256 or 64 x 128 tiles
+ * (large, grouped and large-N small-M products with every K % 256 == 0) or
+ * one-wave 128 x 128 tiles (every K a multiple of 128), those kernels read the
+ * blocked scales directly.  Otherwise the scales are first converted to the
+ * plain layout inside the library's per-stream device workspace (so the call
+ * may allocate it, and returns NOT_SUPPORTED inside a stream capture if it
+ * would have to) and the plain path runs.  Either way C is bitwise what
+ * nvfp4_gemm gives for the same scales.  Other arguments, limits and errors as
+ * for the plain entry points. */
 nvfp4_status nvfp4_gemm_blocked(const void *A, const void *SFA, const void *B, const void *SFB,
                                 void *C, int M, int N, int K, hipStream_t stream);
 nvfp4_status nvfp4_group_gemm_blocked(const nvfp4_problem *problems, int num_groups,

@@ -952,3 +952,58 @@ def test_group_small_m_wide_tile(lib):
             continue
         c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
         assert_parity(got, c16, bound, "small-M wide group %d" % i)
+
+
+@pytest.mark.parametrize("M,N,K,kernel", [
+    (2537, 4100, 1280, 4),   # 128 x 256 tiles, ragged, the tail tiles' K split in three
+    (2200, 4096, 7168, 4),   # 288 tiles, 32 split in four
+    (33, 30000, 1280, 5),    # 64 x 128 small-M tiles, ragged M and N
+    (64, 28672, 4096, 5),
+])
+def test_shared_decode_tiles_read_blocked_scales(lib, M, N, K, kernel):
+    """The shared-decode tiles read blocked scales directly (each wave its
+    rows' dwords of the 512-byte atoms, padding rows included): bitwise the
+    plain call's C, and within the oracle's tolerance."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] == kernel
+    p = inputs.draw_problems(6500 + M + K, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    plain = bits(C)
+    C2 = poisoned(M, N)
+    lib.nvfp4_gemm_blocked(A, blocked_dev(p.SFA, M, K), B, blocked_dev(p.SFB, N, K), C2, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(C2), plain), "blocked scales change C"
+    if M * N <= 4_000_000:
+        c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+        assert_parity(plain, c16, bound, "blocked shared-decode %dx%dx%d" % (M, N, K))
+    else:
+        check_sampled(plain, p, 6501 + K, "blocked shared-decode %dx%dx%d" % (M, N, K), plan_tile(lib, M, N, K))
+
+
+@pytest.mark.parametrize("index", [2, 3, 4])
+def test_named_workloads_with_blocked_scales(lib, index):
+    """The 8192^3, 8-group MoE and 2-group workloads with blocked scales:
+    bitwise the plain calls (every output compared)."""
+    probs = inputs.draw_workload(index)
+    devs = [dev_problem(p) for p in probs]
+    if len(probs) == 1:
+        p, d = probs[0], devs[0]
+        lib.nvfp4_gemm(*d, M=p.M, N=p.N, K=p.K)
+        torch.cuda.synchronize()
+        plain = [bits(d[4])]
+        C2 = poisoned(p.M, p.N)
+        lib.nvfp4_gemm_blocked(d[0], blocked_dev(p.SFA, p.M, p.K), d[2], blocked_dev(p.SFB, p.N, p.K), C2,
+                               p.M, p.N, p.K)
+        torch.cuda.synchronize()
+        got = [bits(C2)]
+    else:
+        plain = run_group(lib, probs)
+        outs = [poisoned(p.M, p.N) for p in probs]
+        lib.nvfp4_group_gemm_blocked([(d[0], blocked_dev(p.SFA, p.M, p.K), d[2], blocked_dev(p.SFB, p.N, p.K), o,
+                                       p.M, p.N, p.K) for d, p, o in zip(devs, probs, outs)])
+        torch.cuda.synchronize()
+        got = [bits(o) for o in outs]
+    for i, (g_, pl) in enumerate(zip(got, plain)):
+        assert np.array_equal(g_, pl), "%s group %d: blocked differs from plain" % (inputs.WORKLOADS[index].name, i)
