@@ -705,12 +705,15 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
             return s;
         return launch_wide_plan(problems, plan, workspace, stream, true);
     }
-    bool direct = plan.cfg == nvfp4::kTile128x128;
+    // the one-wave 128 x 128 tiles (K % 128 == 0) and the small-M panel
+    // (K % 256 == 0) also read the blocked scales directly
+    const int direct_k = plan.cfg == nvfp4::kTile128x128 ? 128 : plan.cfg == nvfp4::kPanel64x64 ? 256 : 0;
+    bool direct = direct_k > 0;
     for (int g = 0; g < num_groups; ++g)
-        if (!empty_output(problems[g]) && problems[g].K % 128 != 0)
+        if (direct && !empty_output(problems[g]) && problems[g].K % direct_k != 0)
             direct = false;
     if (direct) {
-        plan.cfg = nvfp4::kTile128x128Blocked;
+        plan.cfg = plan.cfg == nvfp4::kTile128x128 ? nvfp4::kTile128x128Blocked : nvfp4::kPanel64x64Blocked;
         return run_plan(problems, plan, stream);
     }
     auto up = [](long long x) { return (x + 255) & ~255LL; };

@@ -78,6 +78,7 @@ enum TileConfig : int {
     kTile128x128Blocked = 6, // one-wave 128 x 128 direct-to-LDS tiles, scales in the blocked layout
     kWide128x256 = 7,   // four waves share a 128 x 256 tile, decoded A exchanged through LDS
     kSkinny64x128 = 8,  // eight waves (4 K-groups of 2) share a 64 x 128 tile, decoded A exchanged
+    kPanel64x64Blocked = 9, // kPanel64x64 reading scales in the blocked layout (every K % 256 == 0)
 };
 
 struct TileShape {
@@ -90,6 +91,7 @@ inline TileShape tile_shape(TileConfig c)
     case kStream64x32:
         return {64, 32, 256};
     case kPanel64x64:
+    case kPanel64x64Blocked:
         return {64, 64, 256};
     case kWide128x256:
         return {128, 256, 256};

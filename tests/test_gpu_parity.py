@@ -1007,3 +1007,52 @@ def test_named_workloads_with_blocked_scales(lib, index):
         got = [bits(o) for o in outs]
     for i, (g_, pl) in enumerate(zip(got, plain)):
         assert np.array_equal(g_, pl), "%s group %d: blocked differs from plain" % (inputs.WORKLOADS[index].name, i)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 7168, 16384),   # the small-M decode-shaped product, K split in two
+    (24, 7168, 8192),    # M <= 32: the one-block form reads only the first dword of each piece
+    (300, 512, 16384),   # five row tiles: both halves of the 128-row atoms, padding rows
+    (63, 7000, 4608),    # ragged N: the last tile's columns past N
+])
+def test_panel_reads_blocked_scales(lib, M, N, K):
+    """The small-M panel kernel reads blocked scales directly (8-byte halves
+    of the atoms' 16-byte lines): bitwise the plain call, and within the
+    oracle's tolerance."""
+    info = lib.gemm_plan(M, N, K)
+    assert info["kernel"] in (1, 2) and (info["tile_m"], info["tile_n"]) == (64, 64)
+    p = inputs.draw_problems(6600 + M + K, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    plain = bits(C)
+    C2 = poisoned(M, N)
+    lib.nvfp4_gemm_blocked(A, blocked_dev(p.SFA, M, K), B, blocked_dev(p.SFB, N, K), C2, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(C2), plain), "blocked scales change C"
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(plain, c16, bound, "blocked panel %dx%dx%d" % (M, N, K))
+
+
+def test_group_panel_reads_blocked_scales(lib):
+    """A grouped panel launch with blocked scales (K 256 to 8192, an empty
+    group and a K = 0 group): bitwise the plain grouped call."""
+    shapes = [(64, 6144, 8192), (40, 4096, 4096), (0, 64, 512), (50, 300, 0), (17, 2304, 256)]
+    info, _ = lib.group_gemm_plan(shapes)
+    assert (info["tile_m"], info["tile_n"]) == (64, 64)
+    probs = inputs.draw_problems(6650, shapes)
+    plain = run_group(lib, probs)
+    devs = [dev_problem(p) for p in probs]
+    outs = [poisoned(p.M, p.N) for p in probs]
+    lib.nvfp4_group_gemm_blocked([(d[0], blocked_dev(p.SFA, p.M, p.K) if p.K else d[1], d[2],
+                                   blocked_dev(p.SFB, p.N, p.K) if p.K else d[3], o, p.M, p.N, p.K)
+                                  for d, p, o in zip(devs, probs, outs)])
+    torch.cuda.synchronize()
+    for i, (o, p) in enumerate(zip(outs, probs)):
+        if p.M == 0 or p.N == 0:
+            continue
+        got = bits(o)
+        assert np.array_equal(got, plain[i]), "blocked group %d differs from the plain call" % i
+        if p.K:
+            c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+            assert_parity(got, c16, bound, "blocked panel group %d" % i)
