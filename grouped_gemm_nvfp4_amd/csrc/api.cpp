@@ -305,15 +305,15 @@ void plan_wide_ranges(const nvfp4_problem *problems, Plan *plan, long long max_w
         whole_only();
 }
 
-// pow2: the power-of-two-scale path (one-wave 128 x 128 tiles on the scaled
-// FP4 MFMA, no K split), which needs K % 128 == 0 and 8-byte aligned scales.
-// allow_wide: the wide 128 x 256 tile may be chosen (the blocked-scale path
-// turns it off, as it reads blocked scales on one-wave 128 x 128 tiles).
 // Largest workspace a plan may ask for (the wide tile's balancing split).
 constexpr long long kMaxPlanWorkspace = 256LL << 20;
 
+// pow2: the power-of-two-scale path (one-wave 128 x 128 tiles on the scaled
+// FP4 MFMA, no K split), which needs K % 128 == 0 and 8-byte aligned scales.
+// max_workspace: the wide tile's balancing split is made only where its
+// partial tiles fit in this many bytes.
 nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan, bool pow2 = false,
-                       bool allow_wide = true, long long max_workspace = kMaxPlanWorkspace)
+                       long long max_workspace = kMaxPlanWorkspace)
 {
     if (num_groups < 0 || num_groups > NVFP4_MAX_GROUPS)
         return NVFP4_ERROR_INVALID_VALUE;
@@ -378,7 +378,7 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
     // kernel's 16 KiB ones save (64 x 7168 x 16384, four slices: 35 vs 28 us),
     // so smaller launches stay on the 64-row kernels.
     bool skinny = false;
-    if (max_m > 32 && max_m <= 64 && allow_wide && wide_ok(problems, num_groups)) {
+    if (max_m > 32 && max_m <= 64 && wide_ok(problems, num_groups)) {
         std::vector<int> prefix_s;
         long long total_s = 0;
         int kt_s = 0;
@@ -418,7 +418,7 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         // 2048 x 2048 x 2048, 128 wide tiles, against four waves per 128 x 128
         // tile), else one wave per 128 x 128 tile (or four, below)
         plan->cfg = nvfp4::kTile128x128;
-        if (allow_wide && wide_ok(problems, num_groups)) {
+        if (wide_ok(problems, num_groups)) {
             std::vector<int> prefix_w;
             long long total_w = 0;
             int kt_w = 0;
@@ -834,7 +834,7 @@ nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, c
     p.N = N;
     p.K = K;
     Plan plan;
-    nvfp4_status s = make_plan(&p, 1, &plan, false, true, kScratchBytes);
+    nvfp4_status s = make_plan(&p, 1, &plan, false, kScratchBytes);
     if (s != NVFP4_OK || plan.total_tiles == 0)
         return s;
     if (plan.workspace_bytes > kScratchBytes)
