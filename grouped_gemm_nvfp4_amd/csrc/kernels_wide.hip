@@ -96,6 +96,11 @@ struct Shape {
 
 typedef __attribute__((address_space(3))) void wide_lds_void;
 
+template <bool B>
+struct EdgeTag {
+    static constexpr bool value = B;
+};
+
 // s_waitcnt with only vmcnt = n (lgkmcnt and expcnt at their maxima); the
 // compiler does not order the loads' LDS writes before later LDS reads, so
 // nothing may move across the wait
@@ -234,72 +239,6 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
         }
     };
 
-    // raw operands of one 64-K group: this lane's 16 packed bytes of its A rows
-    // and of its two B rows, and their scale words (blocks 4 g .. 4 g + 3,
-    // shifted to this lane's half)
-    u32x4 ra[RA], rb0, rb1;
-    uint32_t wa[RA], wb0, wb1;
-    auto read_raw = [&](int kt, int g) {
-        const uint8_t *sb = region + (kt & 1) * kStageBytes;
-        const uint8_t *pq = region + 2 * kStageBytes + ((kt >> 1) & 1) * kPairBytes;
-        // the scale dword of a row for 64-K group g of tile kt
-        auto scale_a = [&](int row) -> uint32_t {
-            if constexpr (kBlocked)
-                return *(const uint32_t *)(pq + kPairA + ((2 * (kt & 1) + g) * kARows + row) * 4);
-            else
-                return *(const uint32_t *)(pq + kPairA + 16 * row + 8 * (kt & 1) + 4 * g);
-        };
-        auto scale_b = [&](int row) -> uint32_t {
-            if constexpr (kBlocked)
-                return *(const uint32_t *)(pq + kPairB + ((2 * (kt & 1) + g) * kBRows + row) * 4);
-            else
-                return *(const uint32_t *)(pq + kPairB + 16 * row + 8 * (kt & 1) + 4 * g);
-        };
-#pragma unroll
-        for (int r = 0; r < RA; ++r) {
-            ra[r] = *(const u32x4 *)(sb + kAOff + tiled::swz(32 * r + l32, 2 * g + h));
-            wa[r] = scale_a(32 * r + l32) >> sh;
-        }
-        rb0 = *(const u32x4 *)(sb + kBOff + tiled::swz(l32, 2 * g + h));
-        rb1 = *(const u32x4 *)(sb + kBOff + tiled::swz(32 + l32, 2 * g + h));
-        wb0 = scale_b(l32) >> sh;
-        wb1 = scale_b(32 + l32) >> sh;
-    };
-
-    // fragments of the current sub-step (A_cur: this wave's row blocks) and of
-    // the next (decoded during the current one)
-    half8_t A_cur[RA][2], B_cur[2][2], A_nx[RA][2], B_nx[2][2];
-    // decode this lane's fragments of half `qq` of the group in ra/rb
-    auto decode = [&](int qq) {
-        const half2_t cb0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb0, 1.0f, false);
-        const half2_t cb1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb1, 1.0f, false);
-        const half2_t sb0 = qq ? bcast_hi(cb0) : bcast_lo(cb0);
-        const half2_t sb1 = qq ? bcast_hi(cb1) : bcast_lo(cb1);
-#pragma unroll
-        for (int r = 0; r < RA; ++r) {
-            const half2_t ca = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa[r], 1.0f, false);
-            const half2_t sa = qq ? bcast_hi(ca) : bcast_lo(ca);
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                A_nx[r][s] = decode8(ra[r][2 * qq + s], sa);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            B_nx[0][s] = decode8(rb0[2 * qq + s], sb0);
-            B_nx[1][s] = decode8(rb1[2 * qq + s], sb1);
-        }
-    };
-    auto put_x = [&](int buf) {
-        if constexpr (CW > 1) {
-#pragma unroll
-            for (int r = 0; r < RA; ++r)
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    *(half8_t *)(xbase + buf * Sh::kXBuf + (RA * cw + r) * kXWave + s * kXStep + lane * 16) =
-                        A_nx[r][s];
-        }
-    };
-
     // accumulators: acc[t][f] is row block (RA cw + t) % RB, column block f of
     // this wave's 64 columns; t < RA are the row blocks this wave decodes
     f32x16 acc[RB][2];
@@ -309,98 +248,195 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
         for (int f = 0; f < 2; ++f)
             acc[t][f] = (f32x16){};
 
-    // one sub-step (32 K): the other column waves' row blocks from exchange
-    // buffer xb (read_x), then the raw read and decode of the next sub-step,
-    // 2 RB x 2 MFMAs, and the next fragments into the other exchange buffer
-    constexpr int kOther = RB - RA;
-    half8_t Ao[kOther > 0 ? kOther : 1][2];
-    auto read_x = [&](int xb) {
+    // Row blocks of the tile that hold rows of A: all RB but in a tile at the
+    // M edge.  There (kEdge) the waves skip the decode, exchange and MFMAs of
+    // the empty row blocks (their accumulators stay zero and are never
+    // stored), so a half-empty tile costs little more than half a tile.
+    const int nrb = min(RB, (M - row0 + 31) / 32);
+    auto run_k = [&](auto edge_tag) {
+        constexpr bool kEdge = decltype(edge_tag)::value;
+        auto live_rb = [&](int i) { return !kEdge || i < nrb; };
+        // raw operands of one 64-K group: this lane's 16 packed bytes of its A rows
+        // and of its two B rows, and their scale words (blocks 4 g .. 4 g + 3,
+        // shifted to this lane's half)
+        u32x4 ra[RA], rb0, rb1;
+        uint32_t wa[RA], wb0, wb1;
+        auto read_raw = [&](int kt, int g) {
+            const uint8_t *sb = region + (kt & 1) * kStageBytes;
+            const uint8_t *pq = region + 2 * kStageBytes + ((kt >> 1) & 1) * kPairBytes;
+            // the scale dword of a row for 64-K group g of tile kt
+            auto scale_a = [&](int row) -> uint32_t {
+                if constexpr (kBlocked)
+                    return *(const uint32_t *)(pq + kPairA + ((2 * (kt & 1) + g) * kARows + row) * 4);
+                else
+                    return *(const uint32_t *)(pq + kPairA + 16 * row + 8 * (kt & 1) + 4 * g);
+            };
+            auto scale_b = [&](int row) -> uint32_t {
+                if constexpr (kBlocked)
+                    return *(const uint32_t *)(pq + kPairB + ((2 * (kt & 1) + g) * kBRows + row) * 4);
+                else
+                    return *(const uint32_t *)(pq + kPairB + 16 * row + 8 * (kt & 1) + 4 * g);
+            };
 #pragma unroll
-        for (int t = RA; t < RB; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                Ao[t - RA][s] = *(const half8_t *)(xbase + xb * Sh::kXBuf + ((RA * cw + t) % RB) * kXWave +
-                                                   s * kXStep + lane * 16);
-    };
-    auto mfmas = [&]() {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int t = 0; t < RA; ++t)
-#pragma unroll
-                for (int f = 0; f < 2; ++f)
-                    acc[t][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A_cur[t][s], B_cur[f][s], acc[t][f], 0, 0, 0);
-#pragma unroll
-            for (int t = RA; t < RB; ++t)
-#pragma unroll
-                for (int f = 0; f < 2; ++f)
-                    acc[t][f] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_f16(Ao[t - RA][s], B_cur[f][s], acc[t][f], 0, 0, 0);
-        }
-    };
-    auto advance = [&]() {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-            for (int r = 0; r < RA; ++r)
-                A_cur[r][s] = A_nx[r][s];
-            B_cur[0][s] = B_nx[0][s];
-            B_cur[1][s] = B_nx[1][s];
-        }
-    };
-    // the exchange needs the workgroup barrier; waves that decode all their
-    // own operands (CW == 1) run on their own
-    auto sync = [&]() {
-        if constexpr (CW > 1)
-            LDS_BARRIER();
-    };
+            for (int r = 0; r < RA; ++r) {
+                if (!live_rb(RA * cw + r))
+                    continue;
+                ra[r] = *(const u32x4 *)(sb + kAOff + tiled::swz(32 * r + l32, 2 * g + h));
+                wa[r] = scale_a(32 * r + l32) >> sh;
+            }
+            rb0 = *(const u32x4 *)(sb + kBOff + tiled::swz(l32, 2 * g + h));
+            rb1 = *(const u32x4 *)(sb + kBOff + tiled::swz(32 + l32, 2 * g + h));
+            wb0 = scale_b(l32) >> sh;
+            wb1 = scale_b(32 + l32) >> sh;
+        };
 
-    // prologue: the range's first two K tiles in flight, the first landed, its
-    // sub-step 0 decoded and exchanged
-    issue(0, kt_lo, true);
-    issue(1, kt_lo + 1, false);
-    WAIT_VM(kLoadsOdd);
-    read_raw(kt_lo, 0);
-    decode(0);
-    put_x(0);
-    advance();
-    sync();
+        // fragments of the current sub-step (A_cur: this wave's row blocks) and of
+        // the next (decoded during the current one)
+        half8_t A_cur[RA][2], B_cur[2][2], A_nx[RA][2], B_nx[2][2];
+        // decode this lane's fragments of half `qq` of the group in ra/rb
+        auto decode = [&](int qq) {
+            const half2_t cb0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb0, 1.0f, false);
+            const half2_t cb1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wb1, 1.0f, false);
+            const half2_t sb0 = qq ? bcast_hi(cb0) : bcast_lo(cb0);
+            const half2_t sb1 = qq ? bcast_hi(cb1) : bcast_lo(cb1);
+#pragma unroll
+            for (int r = 0; r < RA; ++r) {
+                if (!live_rb(RA * cw + r))
+                    continue;
+                const half2_t ca = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wa[r], 1.0f, false);
+                const half2_t sa = qq ? bcast_hi(ca) : bcast_lo(ca);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    A_nx[r][s] = decode8(ra[r][2 * qq + s], sa);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                B_nx[0][s] = decode8(rb0[2 * qq + s], sb0);
+                B_nx[1][s] = decode8(rb1[2 * qq + s], sb1);
+            }
+        };
+        auto put_x = [&](int buf) {
+            if constexpr (CW > 1) {
+#pragma unroll
+                for (int r = 0; r < RA; ++r) {
+                    if (!live_rb(RA * cw + r))
+                        continue;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        *(half8_t *)(xbase + buf * Sh::kXBuf + (RA * cw + r) * kXWave + s * kXStep + lane * 16) =
+                            A_nx[r][s];
+                }
+            }
+        };
 
-    // sub-step u of K tile kt (u = 0..3; PAR = kt % 2), exchange buffer u % 2
-    // holds its fragments.  u = 1, 3: the next group's raw operands are read
-    // (u = 3: from tile kt + 1, waited for first); u = 2: tile kt + 2 is
-    // issued into this tile's stage, whose last read was at u = 1.
+
+        // one sub-step (32 K): the other column waves' row blocks from exchange
+        // buffer xb (read_x), then the raw read and decode of the next sub-step,
+        // 2 RB x 2 MFMAs, and the next fragments into the other exchange buffer
+        constexpr int kOther = RB - RA;
+        half8_t Ao[kOther > 0 ? kOther : 1][2];
+        auto read_x = [&](int xb) {
+#pragma unroll
+            for (int t = RA; t < RB; ++t) {
+                if (!live_rb((RA * cw + t) % RB))
+                    continue;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    Ao[t - RA][s] = *(const half8_t *)(xbase + xb * Sh::kXBuf + ((RA * cw + t) % RB) * kXWave +
+                                                       s * kXStep + lane * 16);
+            }
+        };
+        auto mfmas = [&]() {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int t = 0; t < RA; ++t) {
+                    if (!live_rb(RA * cw + t))
+                        continue;
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+                        acc[t][f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A_cur[t][s], B_cur[f][s], acc[t][f], 0, 0, 0);
+                }
+#pragma unroll
+                for (int t = RA; t < RB; ++t) {
+                    if (!live_rb((RA * cw + t) % RB))
+                        continue;
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+                        acc[t][f] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_f16(Ao[t - RA][s], B_cur[f][s], acc[t][f], 0, 0, 0);
+                }
+            }
+        };
+        auto advance = [&]() {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int r = 0; r < RA; ++r)
+                    if (live_rb(RA * cw + r))
+                        A_cur[r][s] = A_nx[r][s];
+                B_cur[0][s] = B_nx[0][s];
+                B_cur[1][s] = B_nx[1][s];
+            }
+        };
+        // the exchange needs the workgroup barrier; waves that decode all their
+        // own operands (CW == 1) run on their own
+        auto sync = [&]() {
+            if constexpr (CW > 1)
+                LDS_BARRIER();
+        };
+
+        // prologue: the range's first two K tiles in flight, the first landed, its
+        // sub-step 0 decoded and exchanged
+        issue(0, kt_lo, true);
+        issue(1, kt_lo + 1, false);
+        WAIT_VM(kLoadsOdd);
+        read_raw(kt_lo, 0);
+        decode(0);
+        put_x(0);
+        advance();
+        sync();
+
+        // sub-step u of K tile kt (u = 0..3; PAR = kt % 2), exchange buffer u % 2
+        // holds its fragments.  u = 1, 3: the next group's raw operands are read
+        // (u = 3: from tile kt + 1, waited for first); u = 2: tile kt + 2 is
+        // issued into this tile's stage, whose last read was at u = 1.
 #define WIDE_SUBSTEP(U, PAR)                                                                                         \
-    do {                                                                                                             \
-        read_x((U) & 1);                                                                                             \
-        if ((U) == 3) {                                                                                              \
-            WAIT_VM((PAR) == 0 ? kLoadsEven : kLoadsOdd);                                                            \
-            read_raw(kt + 1, 0);                                                                                     \
-        } else if ((U) == 1) {                                                                                       \
-            read_raw(kt, 1);                                                                                         \
-        }                                                                                                            \
-        decode(((U) + 1) & 1);                                                                                       \
-        mfmas();                                                                                                     \
-        put_x(((U) + 1) & 1);                                                                                        \
-        if ((U) == 2)                                                                                                \
-            issue(kt & 1, kt + 2, (PAR) == 0);                                                                       \
-        advance();                                                                                                   \
-        sync();                                                                                                      \
-    } while (0)
+        do {                                                                                                             \
+            read_x((U) & 1);                                                                                             \
+            if ((U) == 3) {                                                                                              \
+                WAIT_VM((PAR) == 0 ? kLoadsEven : kLoadsOdd);                                                            \
+                read_raw(kt + 1, 0);                                                                                     \
+            } else if ((U) == 1) {                                                                                       \
+                read_raw(kt, 1);                                                                                         \
+            }                                                                                                            \
+            decode(((U) + 1) & 1);                                                                                       \
+            mfmas();                                                                                                     \
+            put_x(((U) + 1) & 1);                                                                                        \
+            if ((U) == 2)                                                                                                \
+                issue(kt & 1, kt + 2, (PAR) == 0);                                                                       \
+            advance();                                                                                                   \
+            sync();                                                                                                      \
+        } while (0)
 
-    for (int kt = kt_lo; kt < kt_end; kt += 2) {
-        WIDE_SUBSTEP(0, 0);
-        WIDE_SUBSTEP(1, 0);
-        WIDE_SUBSTEP(2, 0);
-        WIDE_SUBSTEP(3, 0);
-        ++kt;
-        WIDE_SUBSTEP(0, 1);
-        WIDE_SUBSTEP(1, 1);
-        WIDE_SUBSTEP(2, 1);
-        WIDE_SUBSTEP(3, 1);
-        --kt;
-    }
+        for (int kt = kt_lo; kt < kt_end; kt += 2) {
+            WIDE_SUBSTEP(0, 0);
+            WIDE_SUBSTEP(1, 0);
+            WIDE_SUBSTEP(2, 0);
+            WIDE_SUBSTEP(3, 0);
+            ++kt;
+            WIDE_SUBSTEP(0, 1);
+            WIDE_SUBSTEP(1, 1);
+            WIDE_SUBSTEP(2, 1);
+            WIDE_SUBSTEP(3, 1);
+            --kt;
+        }
 #undef WIDE_SUBSTEP
+    };
+    if (nrb == RB)
+        run_k(EdgeTag<false>{});
+    else
+        run_k(EdgeTag<true>{});
 
     // the trailing (out-of-range) loads have landed and every wave is past its
     // last LDS access

@@ -39,7 +39,7 @@ def order_bin(tmp_path_factory):
 
 
 GRIDS = [(1, 1), (3, 5), (8, 8), (64, 32), (32, 12), (3, 12), (33, 16), (7, 9), (16, 5), (40, 24),
-         (1, 64), (64, 1), (2, 36), (24, 16)]
+         (1, 64), (64, 1), (2, 36), (24, 16), (3, 16), (4, 16), (2, 8), (8, 24), (9, 16)]
 
 
 def orders(exe, grids):
@@ -81,3 +81,15 @@ def test_xcd_parts_are_compact(order_bin):
         for start in range(0, len(mine), 64):
             window = mine[start:start + 64]
             assert len({m for m, _ in window}) == 8 and len({n for _, n in window}) == 8
+
+
+def test_few_row_grids_put_each_column_on_one_xcd(order_bin):
+    """Grids of at most 8 tile rows and a multiple of 8 columns: every row tile
+    of a column sits at the same position mod 8 (one XCD), and each XCD
+    receives whole columns."""
+    grids = [(3, 16), (4, 16), (1, 64), (2, 8), (8, 24)]
+    for (tm_count, tn_count), coords in zip(grids, orders(order_bin, grids)):
+        for part in range(8):
+            cols = {n for _, n in coords[part::8]}
+            assert all(n % 8 == part for n in cols), (tm_count, tn_count)
+            assert len(coords[part::8]) == tm_count * len(cols)
