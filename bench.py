@@ -65,6 +65,10 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.25,
+                    help="after the --warmup steps, keep stepping (untimed) until this much wall "
+                         "time has passed, so that the timed steps run at the clock the sustained "
+                         "load settles at (0: exactly --warmup steps)")
     ap.add_argument("--workload", type=int, default=HEADLINE_WORKLOAD,
                     help="index into grouped_gemm_nvfp4_amd.inputs.WORKLOADS (default %d, the "
                          "8192^3 product)" % HEADLINE_WORKLOAD)
@@ -369,17 +373,17 @@ class Bench:
             info = self.g.gemm_plan(*self.shapes[0])
         return info
 
-    def run(self, steps, warmup):
-        """Time `steps` calls after `warmup` untimed ones.  Returns the timing
-        figures: wall clock of the timed region, the mean launch (HIP events on
-        the launch stream around the timed region, divided by the steps), a
-        per-launch event-pair distribution, the host time of one call and the
-        cache-warm mean launch (same operands every step)."""
+    def run(self, steps, warmup, warmup_seconds=0.0):
+        """Time `steps` calls after `warmup` untimed ones (and more untimed
+        ones, doubling, until `warmup_seconds` of wall time have passed).
+        Returns the timing figures: wall clock of the timed region, the mean
+        launch (HIP events on the launch stream around the timed region,
+        divided by the steps), a per-launch event-pair distribution, the host
+        time of one call, the cache-warm mean launch (same operands every
+        step) and the untimed steps run."""
         import torch
         stream = self.stream
-        for i in range(warmup):
-            self.step(i)
-        torch.cuda.synchronize()
+        done = settle_warmup(self.step, warmup, warmup_seconds, torch.cuda.synchronize)
 
         e_start = torch.cuda.Event(enable_timing=True)
         e_end = torch.cuda.Event(enable_timing=True)
@@ -418,7 +422,7 @@ class Bench:
         torch.cuda.synchronize()
         warm_s = w0.elapsed_time(w1) / 1e3 / nwarm
         return {"wall_s": wall, "kern_s": kern_s, "each_us": each_us,
-                "host_us": float(np.median(host)) * 1e6, "warm_s": warm_s}
+                "host_us": float(np.median(host)) * 1e6, "warm_s": warm_s, "warmup_steps_run": done}
 
     def roofline(self, kern_s):
         """Roofline object of the workload's kernel from its mean launch."""
@@ -461,11 +465,32 @@ class Bench:
             "roofline": roof,
             "warm_cache_us": t["warm_s"] * 1e6,
             "warm_cache_tflops": self.flops / t["warm_s"] / 1e12,
+            "warmup_steps_run": t.get("warmup_steps_run"),
         }
 
     def release(self):
         self.sets = None
         self.calls = None
+
+
+def settle_warmup(step, warmup, seconds, sync, clock=None):
+    """Untimed steps before a timed region: `warmup` of them, then more,
+    doubling the count each round (each round ends with `sync`), until
+    `seconds` of wall time have passed since the first.  Returns the steps
+    run."""
+    clock = clock or time.perf_counter
+    t0 = clock()
+    for i in range(warmup):
+        step(i)
+    done = warmup
+    sync()
+    while clock() - t0 < seconds:
+        n = max(1, done)
+        for j in range(n):
+            step(done + j)
+        done += n
+        sync()
+    return done
 
 
 def workload_spec(index, shape, codes):
@@ -488,6 +513,8 @@ def compose(args, wl, seed, copies, flops, t, head, extras, cpu, system):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": t.get("warmup_steps_run", args.warmup),
+        "warmup_min_seconds": args.warmup_seconds,
         "ms_per_step": t["wall_s"] / K * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -548,7 +575,7 @@ def main(argv=None):
                 continue
             wl_i, probs_i, seed_i = workload_spec(i, None, codes)
             bi = Bench(lib, g, b, wl_i, probs_i, seed_i, args)
-            extras[wl_i.name] = bi.summary(bi.run(args.steps, args.warmup))
+            extras[wl_i.name] = bi.summary(bi.run(args.steps, args.warmup, args.warmup_seconds))
             bi.release()
             del bi
             torch.cuda.empty_cache()
@@ -556,7 +583,7 @@ def main(argv=None):
 
     wl, probs, seed = workload_spec(args.workload, shape, codes)
     bh = Bench(lib, g, b, wl, probs, seed, args)
-    t = bh.run(args.steps, args.warmup)
+    t = bh.run(args.steps, args.warmup, args.warmup_seconds)
     head = bh.summary(t)
     clock = sample_gfx_clock(bh.step, args.clock_seconds) if args.clock_seconds > 0 else None
 

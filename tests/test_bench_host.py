@@ -51,6 +51,7 @@ def test_default_headline_is_the_large_workload():
     assert args.workload == bench.HEADLINE_WORKLOAD
     assert inputs.WORKLOADS[args.workload].name == "gemm_large_8192x8192x8192"
     assert args.gpus == 1 and not args.no_extras
+    assert args.warmup == 10 and args.warmup_seconds > 0
 
 
 def _fake_bench(index):
@@ -70,7 +71,8 @@ def _fake_bench(index):
 def _fake_timing(kern_us):
     import numpy as np
     return {"wall_s": kern_us * 1e-6 * 20 * 1.05, "kern_s": kern_us * 1e-6,
-            "each_us": np.full(20, kern_us), "host_us": 5.0, "warm_s": kern_us * 0.9e-6}
+            "each_us": np.full(20, kern_us), "host_us": 5.0, "warm_s": kern_us * 0.9e-6,
+            "warmup_steps_run": 40}
 
 
 def test_output_line_carries_every_field():
@@ -94,7 +96,7 @@ def test_output_line_carries_every_field():
               "affinity_cores": bench.affinity_cores(), "omp_num_threads": None}
     out = bench.compose(args, fb.wl, fb.seed, fb.copies, fb.flops, _fake_timing(900.0), head, extras,
                         cpu, system)
-    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "warmup_steps_run", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline", "pct_fp4_peak", "pct_fp16_peak", "workloads", "system"):
         assert key in out, key
@@ -140,3 +142,25 @@ def test_metadata_helpers():
     assert bench.affinity_cores() >= 1
     v = bench.rocm_version()
     assert v is None or v[0].isdigit()
+
+
+def test_settle_warmup_runs_until_the_time_has_passed():
+    """The untimed steps after --warmup double until --warmup-seconds of wall
+    time have passed; with 0 seconds exactly --warmup steps run."""
+    calls, syncs = [], []
+    now = {"t": 0.0}
+
+    def clock():
+        return now["t"]
+
+    def step(i):
+        calls.append(i)
+        now["t"] += 0.001  # one step takes a millisecond
+
+    assert bench.settle_warmup(step, 10, 0.0, lambda: syncs.append(1), clock) == 10
+    assert calls == list(range(10)) and len(syncs) == 1
+    calls.clear()
+    now["t"] = 0.0
+    done = bench.settle_warmup(step, 10, 0.05, lambda: None, clock)
+    assert calls == list(range(done))           # consecutive step indices
+    assert done == 80                            # 10 -> 20 -> 40 -> 80 steps: 80 ms >= 50 ms
