@@ -937,9 +937,10 @@ def test_wide_tile_group_with_empty_and_zero_k(lib):
 
 def test_group_small_m_wide_tile(lib):
     """A grouped launch on the 64 x 128 small-M tile: ragged groups, a K = 0
-    group (zero C), an empty group, different K."""
+    group (zero C), an empty group, different K, and groups of at most 32
+    rows (M-edge tiles whose second row block is skipped)."""
     shapes = [(64, 8192, 2048), (40, 8192, 4096), (50, 8000, 1024), (64, 300, 0), (0, 128, 256),
-              (64, 320, 2048)]
+              (64, 320, 2048), (17, 4096, 2048), (32, 1000, 1024)]
     info, _ = lib.group_gemm_plan(shapes)
     assert info["kernel"] == 5 and info["split_k"] == 1
     probs = inputs.draw_problems(40, shapes)
@@ -956,7 +957,7 @@ def test_group_small_m_wide_tile(lib):
 
 @pytest.mark.parametrize("M,N,K,kernel", [
     (2537, 4100, 1280, 4),   # 128 x 256 tiles, ragged, the tail tiles' K split in three
-    (2200, 4096, 7168, 4),   # 288 tiles, 32 split in four
+    (2200, 4096, 7168, 4),   # 288 tiles, 32 split in four; M-edge tiles of one row block
     (33, 30000, 1280, 5),    # 64 x 128 small-M tiles, ragged M and N
     (64, 28672, 4096, 5),
 ])
