@@ -191,9 +191,11 @@ nvfp4_status nvfp4_scales_from_blocked(const void *blocked, void *sf, int rows, 
 /* nvfp4_gemm / nvfp4_group_gemm with SFA and SFB in the blocked layout
  * (16-byte aligned, nvfp4_blocked_scale_bytes(M or N, K) bytes each).  Where
  * the plain call would run the shared-decode 128 x 256 or 64 x 128 tiles
- * (large, grouped and large-N small-M products with every K % 256 == 0) or
- * one-wave 128 x 128 tiles (every K a multiple of 128), those kernels read the
- * blocked scales directly.  Otherwise the scales are first converted to the
+ * (large, grouped and large-N small-M products with every K % 256 == 0), the
+ * 64 x 64 small-M panel tiles (every K % 256 == 0) or one-wave 128 x 128 tiles
+ * (every K a multiple of 128), those kernels read the blocked scales directly.
+ * Otherwise (the 64 x 32 small-M tiles, four waves per 128 x 128 tile, or K
+ * not a multiple of those steps) the scales are first converted to the
  * plain layout inside the library's per-stream device workspace (so the call
  * may allocate it, and returns NOT_SUPPORTED inside a stream capture if it
  * would have to) and the plain path runs.  Either way C is bitwise what
@@ -231,7 +233,8 @@ nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_g
 /* ---- Allocation-free single GEMM.  For callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, layouts, results (bitwise those of
- * nvfp4_gemm) and errors as nvfp4_gemm, with the same plan and kernels; the
+ * nvfp4_gemm but for the one planning difference below) and errors as
+ * nvfp4_gemm, with the same plan and kernels; the
  * calls that split K keep their tile counters and partial sums in a scratch
  * array of NVFP4_NOALLOC_SCRATCH_BYTES bytes that the library holds in device
  * memory on each GPU it runs on, until the process ends.  The call allocates
@@ -240,9 +243,10 @@ nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_g
  * on any stream.  One difference in planning: where nvfp4_gemm would split the
  * K of some 128 x 256 tiles for balance and their partial tiles would not fit
  * the array, this call keeps those tiles whole; C then differs from
- * nvfp4_gemm's only by fp32 summation order, within the same accuracy bound.  Every call on a GPU shares that GPU's array: calls that
- * overlap in time on one GPU (other streams, concurrent graph replays) race
- * and give wrong results.  A plan whose workspace would exceed the array
+ * nvfp4_gemm's only by fp32 summation order, within the same accuracy bound.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (other streams, concurrent graph replays) race and give wrong
+ * results.  A plan whose workspace would exceed the array
  * returns NVFP4_ERROR_NOT_SUPPORTED (the planner keeps the K-split launches
  * of small products at 256 workgroups of at most 32 KiB of partial sums,
  * within it). */
