@@ -283,6 +283,41 @@ def test_random_shapes_across_planner_regimes(lib, M, N, K):
         check_sampled(run_gemm(lib, p), p, 9101 + N, "random %dx%dx%d" % (M, N, K), plan_tile(lib, M, N, K))
 
 
+def _random_moe_groups():
+    """Seeded mixture-of-experts-like group lists: ragged row counts (M-edge
+    tiles of every kind), one N and K per list, enough 128 x 256 tiles for
+    the wide route."""
+    rng = np.random.default_rng(2025)
+    cases = []
+    for _ in range(3):
+        G = int(rng.integers(5, 11))
+        N = int(rng.choice([2048, 3072, 4096]))
+        K = 256 * int(rng.integers(4, 24))
+        cases.append([(int(rng.integers(1, 700)), N, K) for _ in range(G)])
+    return cases
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_random_moe_groups_on_the_wide_tile(lib, case):
+    """Random MoE-like grouped launches on the 128 x 256 tile: striped tile
+    orders, M-edge tiles with one to three live row blocks, and the balancing
+    split, every group checked against the oracle."""
+    shapes = _random_moe_groups()[case]
+    info, _ = lib.group_gemm_plan(shapes)
+    while info["kernel"] != 4:   # grow every group until the launch has 256 wide tiles
+        shapes = [(M + 128, N, K) for (M, N, K) in shapes]
+        info, _ = lib.group_gemm_plan(shapes)
+    assert info["kernel"] == 4
+    probs = inputs.draw_problems(9300 + case, shapes)
+    outs = run_group(lib, probs)
+    for i, (p, got) in enumerate(zip(probs, outs)):
+        if p.M * p.N <= 1_000_000:
+            c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, p.M, p.N, p.K)
+            assert_parity(got, c16, bound, "moe case %d group %d" % (case, i))
+        else:
+            check_sampled(got, p, 9310 + i, "moe case %d group %d" % (case, i), (128, 256))
+
+
 def test_few_tiles_deterministic(lib):
     """The last arriver adds the K slices in slice order, so repeated calls
     agree bit for bit whatever order the workgroups finish in."""
