@@ -705,15 +705,19 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
             return s;
         return launch_wide_plan(problems, plan, workspace, stream, true);
     }
-    // the one-wave 128 x 128 tiles (K % 128 == 0) and the small-M panel
-    // (K % 256 == 0) also read the blocked scales directly
-    const int direct_k = plan.cfg == nvfp4::kTile128x128 ? 128 : plan.cfg == nvfp4::kPanel64x64 ? 256 : 0;
+    // the one-wave 128 x 128 tiles (K % 128 == 0) and the small-M panel and
+    // stream tiles (K % 256 == 0) also read the blocked scales directly
+    const int direct_k = plan.cfg == nvfp4::kTile128x128                                      ? 128
+                         : (plan.cfg == nvfp4::kPanel64x64 || plan.cfg == nvfp4::kStream64x32) ? 256
+                                                                                               : 0;
     bool direct = direct_k > 0;
     for (int g = 0; g < num_groups; ++g)
         if (direct && !empty_output(problems[g]) && problems[g].K % direct_k != 0)
             direct = false;
     if (direct) {
-        plan.cfg = plan.cfg == nvfp4::kTile128x128 ? nvfp4::kTile128x128Blocked : nvfp4::kPanel64x64Blocked;
+        plan.cfg = plan.cfg == nvfp4::kTile128x128 ? nvfp4::kTile128x128Blocked
+                   : plan.cfg == nvfp4::kPanel64x64 ? nvfp4::kPanel64x64Blocked
+                                                    : nvfp4::kStream64x32Blocked;
         return run_plan(problems, plan, stream);
     }
     auto up = [](long long x) { return (x + 255) & ~255LL; };

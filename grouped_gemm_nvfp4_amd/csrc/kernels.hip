@@ -357,9 +357,16 @@ struct StreamSlot {
 // kVec: K % 256 == 0 and both scale arrays 16-byte aligned: a row's 16 scale
 // bytes of a K tile are one aligned load.  Otherwise they are 8 two-byte
 // loads (K % 32 == 0 makes each pair of blocks wholly inside or past K).
-template <bool kVec>
+//
+// kBlocked (with kVec): SFA and SFB in the blocked layout (512-byte atoms of
+// 128 rows x 4 blocks, row r's block c of an atom at (r % 32) * 16 + (r / 32)
+// * 4 + c).  A row's 16 scale bytes of a K tile are then one dword of each of
+// the tile's four atoms: four 4-byte loads per operand, the tile's 64 A rows
+// being one half of an atom's rows and its 32 B rows one quarter.
+template <bool kVec, bool kBlocked>
 __global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float *partials, int *counters)
 {
+    static_assert(kVec || !kBlocked, "blocked scales need K % 256 == 0");
     using namespace stream;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kWaveBytes];
     __shared__ int s_last;
@@ -400,14 +407,23 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float 
     // rows past M / N read as zero (beyond num_records)
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(d.A + (long)row0 * kb_row, (uint64_t)(M - row0) * kb_row);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(d.B + (long)col0 * kb_row, (uint64_t)(N - col0) * kb_row);
-    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
+    // blocked: the 128-row atom band of the tile's rows (K / 64 atoms)
+    const int rest_k = K / 64;
+    const __amdgpu_buffer_rsrc_t rSA =
+        kBlocked ? make_rsrc(d.SFA + (long)(row0 >> 7) * rest_k * 512, (uint64_t)rest_k * 512)
+                 : make_rsrc(d.SFA + (long)row0 * ks_row, (uint64_t)(M - row0) * ks_row);
+    const __amdgpu_buffer_rsrc_t rSB =
+        kBlocked ? make_rsrc(d.SFB + (long)(col0 >> 7) * rest_k * 512, (uint64_t)rest_k * 512)
+                 : make_rsrc(d.SFB + (long)col0 * ks_row, (uint64_t)(N - col0) * ks_row);
 
     // loop-invariant offsets: line loads cover rows 8j + lane/8, bytes 16 (lane%8)
     const int lrow = lane >> 3, c16 = lane & 7;
     const uint32_t line_off = (uint32_t)(lrow * kb_row + c16 * 16);
-    const uint32_t sfa_off = (uint32_t)(lane * ks_row);
-    const uint32_t sfb_off = (uint32_t)(l32 * ks_row);
+    // plain: row lane (A) / l32 (B) of the [rows][K/16] matrix; blocked: the
+    // row's dword in an atom (A rows row0 % 128 + lane, B rows col0 % 128 + l32)
+    const uint32_t sfa_off = kBlocked ? (uint32_t)((lane & 31) * 16 + (((row0 & 127) >> 5) + (lane >> 5)) * 4)
+                                      : (uint32_t)(lane * ks_row);
+    const uint32_t sfb_off = kBlocked ? (uint32_t)(l32 * 16 + ((col0 & 127) >> 5) * 4) : (uint32_t)(l32 * ks_row);
 
     auto load = [&](StreamSlot &s, int kt) {
         const bool live = kt < kt1;
@@ -421,7 +437,15 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float 
         for (int j = 0; j < 4; ++j)
             s.b[j] = __builtin_amdgcn_raw_buffer_load_b128(
                 rB, cin ? line_off + (uint32_t)(8 * j * kb_row + kb) : kOutOfRange, 0, 0);
-        if (kVec) {
+        if (kBlocked) {
+            // dword j of the row's 16 bytes: atom 4 kt + j
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t at = (uint32_t)((4 * kt + j) * 512);
+                s.sfa[j] = __builtin_amdgcn_raw_buffer_load_b32(rSA, live ? at + sfa_off : kOutOfRange, 0, 0);
+                s.sfb[j] = __builtin_amdgcn_raw_buffer_load_b32(rSB, live ? at + sfb_off : kOutOfRange, 0, 0);
+            }
+        } else if (kVec) {
             s.sfa = __builtin_amdgcn_raw_buffer_load_b128(rSA, live ? sfa_off + ks : kOutOfRange, 0, 0);
             s.sfb = __builtin_amdgcn_raw_buffer_load_b128(rSB, live ? sfb_off + ks : kOutOfRange, 0, 0);
         } else {
@@ -1028,7 +1052,7 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         for (int g = 0; g < table.num_groups; ++g)
             vec = vec && (table.g[g].K % stream::BK) == 0 &&
                   ((((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15) == 0;
-        const void *fn = vec ? (const void *)gemm_stream_kernel<true> : (const void *)gemm_stream_kernel<false>;
+        const void *fn = vec ? (const void *)gemm_stream_kernel<true, false> : (const void *)gemm_stream_kernel<false, false>;
         return hipLaunchKernel(fn, dim3(total), dim3(stream::kThreads), args, 0, stream);
     }
     case kPanel64x64: {
@@ -1043,6 +1067,14 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspa
         const void *fn = half ? (vec ? (const void *)gemm_panel_kernel<true, 1, false> : (const void *)gemm_panel_kernel<false, 1, false>)
                               : (vec ? (const void *)gemm_panel_kernel<true, 2, false> : (const void *)gemm_panel_kernel<false, 2, false>);
         return hipLaunchKernel(fn, dim3(total), dim3(panel::kThreads), args, 0, stream);
+    }
+    case kStream64x32Blocked: {
+        // blocked scales: every K % 256 == 0 and SFA, SFB 16-byte aligned
+        for (int g = 0; g < table.num_groups; ++g)
+            if (table.g[g].K % stream::BK != 0 || (((uintptr_t)table.g[g].SFA) | ((uintptr_t)table.g[g].SFB)) & 15)
+                return hipErrorInvalidValue;
+        return hipLaunchKernel((const void *)gemm_stream_kernel<true, true>, dim3(total), dim3(stream::kThreads), args,
+                               0, stream);
     }
     case kPanel64x64Blocked: {
         // blocked scales: every K % 256 == 0 and SFA, SFB 16-byte aligned

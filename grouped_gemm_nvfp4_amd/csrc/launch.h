@@ -79,6 +79,7 @@ enum TileConfig : int {
     kWide128x256 = 7,   // four waves share a 128 x 256 tile, decoded A exchanged through LDS
     kSkinny64x128 = 8,  // eight waves (4 K-groups of 2) share a 64 x 128 tile, decoded A exchanged
     kPanel64x64Blocked = 9, // kPanel64x64 reading scales in the blocked layout (every K % 256 == 0)
+    kStream64x32Blocked = 10, // kStream64x32 reading scales in the blocked layout (every K % 256 == 0)
 };
 
 struct TileShape {
@@ -89,6 +90,7 @@ inline TileShape tile_shape(TileConfig c)
 {
     switch (c) {
     case kStream64x32:
+    case kStream64x32Blocked:
         return {64, 32, 256};
     case kPanel64x64:
     case kPanel64x64Blocked:

@@ -192,10 +192,10 @@ nvfp4_status nvfp4_scales_from_blocked(const void *blocked, void *sf, int rows, 
  * (16-byte aligned, nvfp4_blocked_scale_bytes(M or N, K) bytes each).  Where
  * the plain call would run the shared-decode 128 x 256 or 64 x 128 tiles
  * (large, grouped and large-N small-M products with every K % 256 == 0), the
- * 64 x 64 small-M panel tiles (every K % 256 == 0) or one-wave 128 x 128 tiles
- * (every K a multiple of 128), those kernels read the blocked scales directly.
- * Otherwise (the 64 x 32 small-M tiles, four waves per 128 x 128 tile, or K
- * not a multiple of those steps) the scales are first converted to the
+ * 64 x 64 and 64 x 32 small-M tiles (every K % 256 == 0) or one-wave
+ * 128 x 128 tiles (every K a multiple of 128), those kernels read the blocked
+ * scales directly.  Otherwise (four waves per 128 x 128 tile, or K not a
+ * multiple of those steps) the scales are first converted to the
  * plain layout inside the library's per-stream device workspace (so the call
  * may allocate it, and returns NOT_SUPPORTED inside a stream capture if it
  * would have to) and the plain path runs.  Either way C is bitwise what

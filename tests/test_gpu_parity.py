@@ -634,7 +634,7 @@ def blocked_dev(sf, rows, K):
 
 @pytest.mark.parametrize("M,N,K", [
     (64, 6144, 8192),    # panel kernel with a K split (tile counters in the workspace)
-    (40, 500, 1024),     # stream kernel
+    (40, 500, 1024),     # stream kernel (reads the blocked scales directly)
     (300, 260, 2080),    # few tiles with M > 64, ragged K tile: converted scales
 ])
 def test_gemm_blocked_equals_plain(lib, M, N, K):
@@ -1068,6 +1068,30 @@ def test_panel_reads_blocked_scales(lib, M, N, K):
     assert np.array_equal(bits(C2), plain), "blocked scales change C"
     c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
     assert_parity(plain, c16, bound, "blocked panel %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 2048, 2048),    # 64 x 32 tiles, K split in two
+    (200, 640, 4096),    # four row tiles: both halves of the first atom band, and the second band
+    (17, 3000, 1024),    # ragged N: the last tile's columns past N; a quarter of an atom per B tile
+])
+def test_stream_reads_blocked_scales(lib, M, N, K):
+    """The 64 x 32 stream tiles read blocked scales directly (one dword of
+    each of a K tile's four atoms per row): bitwise the plain call, and within
+    the oracle's tolerance."""
+    info = lib.gemm_plan(M, N, K)
+    assert (info["tile_m"], info["tile_n"]) == (64, 32)
+    p = inputs.draw_problems(6700 + M + K, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    plain = bits(C)
+    C2 = poisoned(M, N)
+    lib.nvfp4_gemm_blocked(A, blocked_dev(p.SFA, M, K), B, blocked_dev(p.SFB, N, K), C2, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(C2), plain), "blocked scales change C"
+    c16, _, bound = oracle.gemm(p.A, p.SFA, p.B, p.SFB, M, N, K)
+    assert_parity(plain, c16, bound, "blocked stream %dx%dx%d" % (M, N, K))
 
 
 def test_group_panel_reads_blocked_scales(lib):
