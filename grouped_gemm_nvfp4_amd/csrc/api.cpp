@@ -1056,7 +1056,12 @@ nvfp4_status nvfp4_release_workspaces(void)
 
 const char *nvfp4_status_string(nvfp4_status status)
 {
-    switch (status) {
+    // a C caller may pass any int: read the bits as one (an out-of-range value
+    // is not a valid C++ enum value)
+    static_assert(sizeof(nvfp4_status) == sizeof(int), "the status enum is an int");
+    int code = 0;
+    memcpy(&code, &status, sizeof(code));
+    switch (code) {
     case NVFP4_OK:
         return "NVFP4_OK";
     case NVFP4_ERROR_INVALID_VALUE:
