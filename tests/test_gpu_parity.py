@@ -258,7 +258,7 @@ def test_few_tiles_take_64_row_kernels(lib, M, N, K):
 def _random_regime_shapes():
     rng = np.random.default_rng(2024)
     shapes = []
-    for regime in range(4):
+    for regime in range(6):
         for _ in range(2):
             if regime == 0:    # M <= 64
                 shapes.append((int(rng.integers(1, 65)), int(rng.integers(1, 9000)), 32 * int(rng.integers(1, 400))))
@@ -266,8 +266,12 @@ def _random_regime_shapes():
                 shapes.append((int(rng.integers(65, 1600)), int(rng.integers(1, 1600)), 32 * int(rng.integers(1, 300))))
             elif regime == 2:  # many tiles, K % 128 == 0
                 shapes.append((int(rng.integers(1000, 4200)), int(rng.integers(1000, 4200)), 128 * int(rng.integers(1, 24))))
-            else:              # many tiles, K % 256 == 0 (scales two K tiles per load)
+            elif regime == 3:  # many tiles, K % 256 == 0 (scales two K tiles per load)
                 shapes.append((int(rng.integers(1500, 3500)), int(rng.integers(1500, 3500)), 256 * int(rng.integers(1, 12))))
+            elif regime == 4:  # the 128 x 256 wide tile, its balancing split and M-edge tiles
+                shapes.append((int(rng.integers(2048, 5000)), int(rng.integers(2048, 5000)), 256 * int(rng.integers(1, 16))))
+            else:              # 32 < M <= 64 with many columns: the 64 x 128 small-M tile
+                shapes.append((int(rng.integers(33, 65)), int(rng.integers(24600, 40000)), 256 * int(rng.integers(2, 16))))
     return shapes
 
 
