@@ -130,11 +130,16 @@ Workspaces &workspaces()
     return *w;
 }
 
+// A library workspace: the tile counters (zero), the pair slots (every one
+// kPairSentinel), then the partial tiles, all at fixed offsets.  Calls leave
+// the counters zero and the pair slots at the sentinel, so these states hold
+// from one call to the next.
 nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
 {
     *out = nullptr;
     if (bytes == 0)
         return NVFP4_OK;
+    bytes = std::max(bytes, (size_t)nvfp4::kPartialsOffset);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return NVFP4_ERROR_LAUNCH;
@@ -157,8 +162,11 @@ nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
     void *p = nullptr;
     if (hipMalloc(&p, rounded) != hipSuccess)
         return NVFP4_ERROR_LAUNCH;
-    // the tile counters start at zero (stream order puts this before any use)
-    if (hipMemsetAsync(p, 0, (size_t)nvfp4::kCounterBytes, stream) != hipSuccess) {
+    // the tile counters start at zero and the pair slots at the sentinel
+    // (stream order puts this before any use)
+    if (hipMemsetAsync(p, 0, (size_t)nvfp4::kCounterBytes, stream) != hipSuccess ||
+        hipMemsetD32Async((hipDeviceptr_t)((char *)p + nvfp4::kCounterBytes), (int)nvfp4::kPairSentinel,
+                          (size_t)(nvfp4::kPairSlotBytes / 4), stream) != hipSuccess) {
         (void)hipFree(p);
         return NVFP4_ERROR_LAUNCH;
     }
@@ -167,6 +175,23 @@ nvfp4_status get_workspace(size_t bytes, hipStream_t stream, void **out)
     e = std::make_pair(p, rounded);
     *out = p;
     return NVFP4_OK;
+}
+
+// Where a launch finds its K-split state.  pairs is null where the pair
+// slots are not kept (the two-slice launches then take the ticket protocol).
+struct WorkspaceView {
+    int *counters;
+    uint32_t *pairs;
+    float *partials;
+};
+
+// The view of a library workspace (or of none).
+WorkspaceView library_view(void *ws)
+{
+    if (ws == nullptr)
+        return {nullptr, nullptr, nullptr};
+    char *b = (char *)ws;
+    return {(int *)b, (uint32_t *)(b + nvfp4::kCounterBytes), (float *)(b + nvfp4::kPartialsOffset)};
 }
 
 // Workgroups that keep every compute unit of an MI355X busy.
@@ -300,7 +325,7 @@ void plan_wide_ranges(const nvfp4_problem *problems, Plan *plan, long long max_w
             slots += (long long)(t - w) * s;
         }
     }
-    const long long ws = slots > 0 ? nvfp4::kCounterBytes + slots * nvfp4::kWidePartialBytes : 0;
+    const long long ws = slots > 0 ? nvfp4::kPartialsOffset + slots * nvfp4::kWidePartialBytes : 0;
     if (split_tiles > nvfp4::kMaxSplitTiles || ws > max_workspace)
         whole_only();
 }
@@ -497,7 +522,7 @@ nvfp4_status make_plan(const nvfp4_problem *problems, int num_groups, Plan *plan
         }
         plan->split_k = max_split;
         plan->workgroups = wgs;
-        plan->workspace_bytes = slots > 0 ? nvfp4::kCounterBytes + slots * nvfp4::kWidePartialBytes : 0;
+        plan->workspace_bytes = slots > 0 ? nvfp4::kPartialsOffset + slots * nvfp4::kWidePartialBytes : 0;
     }
     return NVFP4_OK;
 }
@@ -517,11 +542,11 @@ void fill_info(const Plan &plan, nvfp4_plan_info *info)
     info->workspace_bytes = plan.workspace_bytes;
 }
 
-// Launches a finished plan with its workspace (plan.workspace_bytes at
-// `workspace`, counters zero): groups in plan order, kMaxGroupsPerLaunch per
+// Launches a finished plan with its workspace (counters zero, partial tiles
+// room for the plan's split): groups in plan order, kMaxGroupsPerLaunch per
 // launch.
 // blocked: SFA and SFB of every problem are in the blocked layout
-nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream,
+nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, WorkspaceView ws, hipStream_t stream,
                               bool blocked = false)
 {
     const nvfp4::TileShape ts = nvfp4::tile_shape(plan.cfg);
@@ -541,7 +566,7 @@ nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, v
         table.tile_cols = bn;
         table.blocked = blocked ? 1 : 0;
         // launches of one call share the workspace: stream order keeps them apart
-        const hipError_t e = nvfp4::launch_wide(table, workspace, stream);
+        const hipError_t e = nvfp4::launch_wide(table, ws.counters, ws.partials, stream);
         n = 0;
         cnt = 0;
         slot = 0;
@@ -579,21 +604,25 @@ nvfp4_status launch_wide_plan(const nvfp4_problem *problems, const Plan &plan, v
     return flush();
 }
 
-nvfp4_status launch_plan(const nvfp4_problem *problems, const Plan &plan, void *workspace, hipStream_t stream)
+nvfp4_status launch_plan(const nvfp4_problem *problems, const Plan &plan, WorkspaceView ws, hipStream_t stream)
 {
     if (plan.cfg == nvfp4::kWide128x256 || plan.cfg == nvfp4::kSkinny64x128)
-        return launch_wide_plan(problems, plan, workspace, stream);
+        return launch_wide_plan(problems, plan, ws, stream);
     nvfp4_status s = NVFP4_OK;
     GroupTable table;
     memset(&table, 0, sizeof(table));
     table.split_k = plan.split_k;
+    // two-slice panel launches sum through the pair slots (the stream tile's
+    // sixteen-byte partial stores keep the ticket protocol faster)
+    const bool panel = plan.cfg == nvfp4::kPanel64x64 || plan.cfg == nvfp4::kPanel64x64Blocked;
+    table.pairs = plan.split_k == 2 && panel ? ws.pairs : nullptr;
     int n = 0;
     auto flush = [&]() -> nvfp4_status {
         if (n == 0)
             return NVFP4_OK;
         table.num_groups = n;
         // launches of one call share the workspace: stream order keeps them apart
-        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, workspace, stream);
+        hipError_t e = nvfp4::launch_grouped(table, plan.cfg, ws.counters, ws.partials, stream);
         n = 0;
         table.prefix[0] = 0;
         return e == hipSuccess ? NVFP4_OK : NVFP4_ERROR_LAUNCH;
@@ -631,7 +660,7 @@ nvfp4_status run_plan(const nvfp4_problem *problems, const Plan &plan, hipStream
     nvfp4_status s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
     if (s != NVFP4_OK)
         return s;
-    return launch_plan(problems, plan, workspace, stream);
+    return launch_plan(problems, plan, library_view(workspace), stream);
 }
 
 nvfp4_status run(const nvfp4_problem *problems, int num_groups, hipStream_t stream, bool pow2 = false)
@@ -682,8 +711,8 @@ nvfp4_status convert_one(const void *src, void *dst, int rows, int K, bool to_bl
 // Grouped product with blocked scales.  Where the plan takes one-wave 128 x
 // 128 tiles and every K is a multiple of 128, that kernel reads the blocked
 // scales directly.  Otherwise the scales are converted to the plain layout in
-// the stream's workspace (after the tile counters and whatever the plan's K
-// split needs), then the plain path runs on the converted copies.
+// the stream's workspace (after the tile counters, the pair slots and whatever
+// the plan's K split needs), then the plain path runs on the converted copies.
 nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStream_t stream)
 {
     Plan plan;
@@ -703,7 +732,7 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
         s = get_workspace((size_t)plan.workspace_bytes, stream, &workspace);
         if (s != NVFP4_OK)
             return s;
-        return launch_wide_plan(problems, plan, workspace, stream, true);
+        return launch_wide_plan(problems, plan, library_view(workspace), stream, true);
     }
     // the one-wave 128 x 128 tiles (K % 128 == 0) and the small-M panel and
     // stream tiles (K % 256 == 0) also read the blocked scales directly
@@ -721,7 +750,7 @@ nvfp4_status run_blocked(const nvfp4_problem *problems, int num_groups, hipStrea
         return run_plan(problems, plan, stream);
     }
     auto up = [](long long x) { return (x + 255) & ~255LL; };
-    const long long base = up(std::max<long long>(plan.workspace_bytes, nvfp4::kCounterBytes));
+    const long long base = up(std::max<long long>(plan.workspace_bytes, nvfp4::kPartialsOffset));
     std::vector<long long> off_a(num_groups, 0), off_b(num_groups, 0);
     long long total = base;
     for (int g = 0; g < num_groups; ++g) {
@@ -837,14 +866,18 @@ nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, c
     p.M = M;
     p.N = N;
     p.K = K;
+    // The scratch holds the tile counters and the partial tiles; it keeps no
+    // pair slots, so two-slice launches take the ticket protocol.  A plan
+    // fits when its library workspace less the pair slots does.
     Plan plan;
-    nvfp4_status s = make_plan(&p, 1, &plan, false, kScratchBytes);
+    nvfp4_status s = make_plan(&p, 1, &plan, false, kScratchBytes + nvfp4::kPairSlotBytes);
     if (s != NVFP4_OK || plan.total_tiles == 0)
         return s;
-    if (plan.workspace_bytes > kScratchBytes)
+    if (plan.workspace_bytes - nvfp4::kPairSlotBytes > kScratchBytes)
         return NVFP4_ERROR_NOT_SUPPORTED;
-    void *ws = nullptr;
+    WorkspaceView view{nullptr, nullptr, nullptr};
     if (plan.workspace_bytes > 0) {
+        void *ws = nullptr;
         s = device_scratch(&ws);
         if (s != NVFP4_OK)
             return s;
@@ -852,8 +885,9 @@ nvfp4_status nvfp4_gemm_noalloc(const void *A, const void *SFA, const void *B, c
         // node in a captured graph), ordered before the GEMM by the stream
         if (nvfp4::launch_clear_words(ws, (int)(nvfp4::kCounterBytes / 4), stream) != hipSuccess)
             return NVFP4_ERROR_LAUNCH;
+        view = {(int *)ws, nullptr, (float *)((char *)ws + nvfp4::kCounterBytes)};
     }
-    return launch_plan(&p, plan, ws, stream);
+    return launch_plan(&p, plan, view, stream);
 }
 
 nvfp4_status nvfp4_gemm(const void *A, const void *SFA, const void *B, const void *SFB,

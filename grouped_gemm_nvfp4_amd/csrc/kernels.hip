@@ -328,6 +328,33 @@ __device__ inline bool add_slices(float (&v)[kN], float *part, int slice_elems, 
     return true;
 }
 
+// Two-slice sum without a ticket (split_k == 2 and pair slots given).  Each
+// thread exchanges each of its kN values into its slot (slot + i * kStride),
+// which holds kPairSentinel until the first of the two slices' exchanges.
+// The exchange that gets a value back is the second one for that element: it
+// adds the two (fp32 addition of two terms is commutative, so the sum does not
+// depend on which slice comes second and equals the slice-ordered sum),
+// restores the sentinel for the next launch, and marks the element as this
+// thread's to write.  The pairing rests only on the atomicity of the two
+// exchanges of one slot (agent scope): the second reads the first's value.
+template <int kN, int kStride>
+__device__ inline void add_pair(float (&v)[kN], bool (&own)[kN], uint32_t *slot)
+{
+    uint32_t old[kN];
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+        old[i] = __hip_atomic_exchange(slot + i * kStride, __float_as_uint(v[i]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+        own[i] = old[i] != kPairSentinel;
+        if (own[i]) {
+            v[i] += __uint_as_float(old[i]);
+            __hip_atomic_store(slot + i * kStride, kPairSentinel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 namespace stream {
 constexpr int BM = 64, BN = 32, BK = 256;
 constexpr int kThreads = 512;
@@ -920,7 +947,14 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
         v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
         v[4] += q.x; v[5] += q.y; v[6] += q.z; v[7] += q.w;
     }
-    if (S > 1) {
+    bool own[8]; // the elements this thread writes
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        own[i] = true;
+    if (S == 2 && tab.pairs != nullptr) {
+        // pair slots, row-major [tile][64][64]
+        add_pair<8, BN>(v, own, tab.pairs + (long)tile * kTileElems + m0 * BN + n);
+    } else if (S > 1) {
         // row-major partial tiles, [tile][slice][64][64]
         if (!add_slices<8, BN>(v, partials + (long)tile * S * kTileElems + m0 * BN + n, kTileElems, S, split,
                                counters + tile, &s_last))
@@ -932,7 +966,7 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = row0 + m0 + i;
-        if (row < M)
+        if (own[i] && row < M)
             d.C[(long)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v[i]);
     }
 }
@@ -1034,16 +1068,17 @@ hipError_t launch_clear_words(void *p, int words, hipStream_t stream)
     return hipLaunchKernel((const void *)clear_words_kernel, dim3(1), dim3(256), args, 0, stream);
 }
 
-hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, hipStream_t stream)
+hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, int *counters, float *partials,
+                          hipStream_t stream)
 {
     const int tiles = table.prefix[table.num_groups];
     const int total = tiles * table.split_k;
     if (total <= 0)
         return hipSuccess;
-    // workspace: tile counters, then the partial tiles
-    int *counters = (int *)workspace;
-    float *partials = workspace ? (float *)((char *)workspace + kCounterBytes) : nullptr;
-    if (table.split_k > 1 && (workspace == nullptr || tiles > kMaxSplitTiles))
+    if (table.split_k > 1 && (counters == nullptr || partials == nullptr || tiles > kMaxSplitTiles))
+        return hipErrorInvalidValue;
+    // the pair slots hold one 64 x 64 tile's elements per tile
+    if (table.pairs != nullptr && table.split_k == 2 && (long long)tiles * 64 * 64 * 4 > kPairSlotBytes)
         return hipErrorInvalidValue;
     void *args[] = {const_cast<GroupTable *>(&table), &partials, &counters};
     switch (cfg) {

@@ -130,7 +130,7 @@ struct EdgeTag {
 // rows' dwords of the pair's four atoms (4-byte direct loads, [atom][row] in
 // the pair buffer) instead of 16 contiguous bytes per row.
 template <int RB, int CW, int KG, bool kBlocked>
-__device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *ws)
+__device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *ws, float *parts)
 {
     using namespace wide;
     using Sh = Shape<RB, CW, KG>;
@@ -444,7 +444,6 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
     LDS_BARRIER();
 
     const int tid = (int)threadIdx.x;
-    float *const parts = (float *)(ws + kCounterBytes);
     const long tile_slot0 = (long)d.slot0 + (long)tile_local * S;
     int *const counter = (int *)ws + d.cnt0 + tile_local;
     // last-arriver protocol of a split tile (every thread calls it after
@@ -640,21 +639,21 @@ __device__ inline void wide_tile(const WideTable &tab, const int wid, uint8_t *w
 
 // 128 x 256 wide tiles: four waves, two workgroups per CU
 template <bool kBlocked>
-__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(WideTable tab, uint8_t *ws)
+__global__ __launch_bounds__(256, 2) void gemm_wide_kernel(WideTable tab, uint8_t *ws, float *parts)
 {
-    wide_tile<4, 4, 1, kBlocked>(tab, (int)blockIdx.x, ws);
+    wide_tile<4, 4, 1, kBlocked>(tab, (int)blockIdx.x, ws, parts);
 }
 
 // 64 x 128 small-M tiles: eight waves (four K-groups of two), one workgroup per CU
 template <bool kBlocked>
-__global__ __launch_bounds__(512, 1) void gemm_skinny_kernel(WideTable tab, uint8_t *ws)
+__global__ __launch_bounds__(512, 1) void gemm_skinny_kernel(WideTable tab, uint8_t *ws, float *parts)
 {
-    wide_tile<2, 2, 4, kBlocked>(tab, (int)blockIdx.x, ws);
+    wide_tile<2, 2, 4, kBlocked>(tab, (int)blockIdx.x, ws, parts);
 }
 
 } // namespace
 
-hipError_t launch_wide(const WideTable &table, void *workspace, hipStream_t stream)
+hipError_t launch_wide(const WideTable &table, void *workspace, float *partials, hipStream_t stream)
 {
     const int wgs = table.prefix[table.num_groups];
     if (wgs <= 0)
@@ -672,12 +671,13 @@ hipError_t launch_wide(const WideTable &table, void *workspace, hipStream_t stre
             d.tiles_n != (d.N + bn - 1) / bn || d.split < 1 || n * d.split != table.prefix[g + 1] - table.prefix[g] ||
             d.tile0 < 0 || (long long)d.tile0 + n > (long long)d.tiles_m * d.tiles_n ||
             (bm == 128 && d.split > kMaxWideSplit) ||
-            (d.split > 1 && (workspace == nullptr || d.split * kg > d.K / (2 * wide::BK) || d.cnt0 < 0 ||
+            (d.split > 1 && (workspace == nullptr || partials == nullptr || d.split * kg > d.K / (2 * wide::BK) ||
+                             d.cnt0 < 0 ||
                              d.cnt0 + n > kMaxSplitTiles || d.slot0 < 0)))
             return hipErrorInvalidValue;
     }
     uint8_t *ws = (uint8_t *)workspace;
-    void *args[] = {const_cast<WideTable *>(&table), &ws};
+    void *args[] = {const_cast<WideTable *>(&table), &ws, &partials};
     if (table.blocked != 0 && table.blocked != 1)
         return hipErrorInvalidValue;
     const bool blocked = table.blocked == 1;

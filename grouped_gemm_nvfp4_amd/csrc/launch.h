@@ -33,9 +33,14 @@ constexpr int kMaxGroupsPerLaunch = 64;
 struct GroupTable {
     int num_groups;
     int split_k;                         // K slices per tile (1: no split)
+    // split_k == 2 on the 64 x 64 panel kernel: the pair slots of the
+    // workspace (kPairSlotBytes, every slot holding kPairSentinel between
+    // launches), or null for the ticket protocol; other kernels ignore it
+    uint32_t *pairs;
     int prefix[kMaxGroupsPerLaunch + 1]; // in output tiles
     GemmDesc g[kMaxGroupsPerLaunch];
 };
+static_assert(sizeof(GroupTable) <= 4096, "kernel-argument budget");
 
 // Device-resident grouped calls: the problem table lives in device memory
 // (written there by the caller, possibly by an earlier kernel), so the host
@@ -117,17 +122,27 @@ inline long long partial_elems(TileConfig c)
 
 // Device workspace of a K-split launch (bytes): kMaxSplitTiles tile counters
 // (zero when the workspace is allocated; a kernel that uses them leaves them
-// zero), then the fp32 partial tiles of every (tile, K slice).  Such launches
-// have at most kMaxSplitTiles tiles.
+// zero), the pair slots of two-slice launches on the panel kernel (one
+// 32-bit slot per output element of at most 128 tiles of 64 x 64, each
+// holding kPairSentinel between launches), then the fp32 partial tiles of
+// every (tile, K slice).  Such launches have at most kMaxSplitTiles tiles.
 constexpr int kMaxSplitTiles = 4096;
 constexpr long long kCounterBytes = kMaxSplitTiles * 4;
+constexpr long long kPairSlotBytes = 128LL * 64 * 64 * 4;
+// A signalling-NaN pattern: fp32 arithmetic never produces it (NaN results
+// are quiet), so no partial sum can be mistaken for an empty slot.
+constexpr uint32_t kPairSentinel = 0x7FBADBADu;
+constexpr long long kPartialsOffset = kCounterBytes + kPairSlotBytes;
 inline long long workspace_bytes(TileConfig c, long long total_tiles, int split_k)
 {
-    return split_k > 1 ? kCounterBytes + total_tiles * split_k * partial_elems(c) * 4 : 0;
+    return split_k > 1 ? kPartialsOffset + total_tiles * split_k * partial_elems(c) * 4 : 0;
 }
 
-// Launches one grouped pass (table already filled, prefix included).
-hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, void *workspace, hipStream_t stream);
+// Launches one grouped pass (table already filled, prefix included).  A
+// K-split launch takes its tile counters at `counters` and its partial tiles
+// at `partials` (and its pair slots at table.pairs, when set).
+hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, int *counters, float *partials,
+                          hipStream_t stream);
 // The direct-to-LDS 128 x 128 kernels (kernels_dma.hip): one wave per tile
 // (kTile128x128, kTile128x128Pow2, kTile128x128Blocked) or four
 // (kTile128x128K4).  Every K % 128 == 0 and the scales 8-byte aligned
@@ -171,8 +186,9 @@ static_assert(sizeof(WideTable) <= 4096, "kernel-argument budget");
 constexpr long long kWidePartialBytes = 128LL * 256 * 4;
 constexpr long long kSkinnyPartialBytes = 64LL * 128 * 4;
 // Checks the contract (every K % 256 == 0; A, B, SFA, SFB 16-byte aligned;
-// the grid sizes; a workspace when some range splits) and launches.
-hipError_t launch_wide(const WideTable &table, void *workspace, hipStream_t stream);
+// the grid sizes; a workspace when some range splits) and launches.  The
+// tile counters are at `workspace`, the partial tiles at `partials`.
+hipError_t launch_wide(const WideTable &table, void *workspace, float *partials, hipStream_t stream);
 
 // Scale-layout conversion, batched: entry e moves the scales of a
 // rows[e] x (kb[e] = K/16) matrix between the plain [rows][K/16] layout and

@@ -246,7 +246,9 @@ nvfp4_status nvfp4_group_gemm_pow2scale(const nvfp4_problem *problems, int num_g
  * nvfp4_gemm's only by fp32 summation order, within the same accuracy bound.
  * Every call on a GPU shares that GPU's array: calls that overlap in time on
  * one GPU (other streams, concurrent graph replays) race and give wrong
- * results.  A plan whose workspace would exceed the array
+ * results.  The array holds no two-slice pair slots: two-slice sums take
+ * the ticket protocol here, with bitwise the same results.  A plan whose
+ * tile counters and partial sums would exceed the array
  * returns NVFP4_ERROR_NOT_SUPPORTED (the planner keeps the K-split launches
  * of small products at 256 workgroups of at most 32 KiB of partial sums,
  * within it). */

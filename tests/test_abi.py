@@ -331,7 +331,9 @@ def test_plan_wide_balance(M, N, K, workgroups, split):
     assert info["kernel"] == 4
     assert info["workgroups"] == workgroups and info["split_k"] == split
     slots = workgroups - (info["total_tiles"] // 256 * 256) if split > 1 else 0
-    assert info["workspace_bytes"] == (16384 + slots * 128 * 256 * 4 if slots else 0)
+    # tile counters (4096 x 4 bytes), the two-slice pair slots (128 tiles of
+    # 64 x 64 words), then one 128 x 256 fp32 partial tile per split slot
+    assert info["workspace_bytes"] == (16384 + 128 * 64 * 64 * 4 + slots * 128 * 256 * 4 if slots else 0)
 
 
 def test_plan_grouped_workloads_take_the_wide_tile():

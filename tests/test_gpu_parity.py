@@ -431,6 +431,51 @@ def test_largest_k_all_positive(lib, M, N, kernel_tile):
                       plan_tile(lib, M, N, K))
 
 
+# ------------------------------------------------- two-slice pair slots
+
+def test_two_slice_pairs_across_interleaved_calls(lib):
+    """Two-slice K splits on the 64 x 64 panel tile sum their slices through
+    the workspace's pair slots, which every such call must leave at their
+    empty state.  On one stream: a two-slice panel call, a two-slice stream
+    call (ticket protocol), a wide-tile call whose K split uses the partial
+    tiles after the pair slots, the same two-slice calls again on new data,
+    and a two-slice grouped panel call; each against the oracle, and the
+    repeated calls bitwise equal to the allocation-free entry point's sums
+    (which keeps no pair slots and takes the ticket protocol)."""
+    panel, stream_, wide = (100, 3072, 4096), (33, 2400, 2048), (2304, 4096, 1024)
+    assert (lib.gemm_plan(*panel)["tile_n"], lib.gemm_plan(*panel)["split_k"]) == (64, 2)
+    assert (lib.gemm_plan(*stream_)["tile_n"], lib.gemm_plan(*stream_)["split_k"]) == (32, 2)
+    info = lib.gemm_plan(*wide)
+    assert info["kernel"] == 4 and info["split_k"] > 1
+    seq = [panel, stream_, wide, panel, stream_]
+    probs = inputs.draw_problems(7700, seq)
+    outs = []
+    for p in probs:
+        A, SFA, B, SFB, C = dev_problem(p)
+        lib.nvfp4_gemm(A, SFA, B, SFB, C, M=p.M, N=p.N, K=p.K)
+        outs.append((C, (A, SFA, B, SFB)))
+    torch.cuda.synchronize()
+    for i, (p, (C, _)) in enumerate(zip(probs, outs)):
+        what = "call %d %dx%dx%d" % (i, p.M, p.N, p.K)
+        if p.M * p.N <= 400_000:
+            check_against_full_oracle(bits(C), p, what)
+        else:
+            check_sampled(bits(C), p, 7701 + i, what, plan_tile(lib, p.M, p.N, p.K))
+    for i in (3, 4):
+        p = probs[i]
+        A, SFA, B, SFB = outs[i][1]
+        C2 = poisoned(p.M, p.N)
+        lib.nvfp4_gemm_noalloc(A, SFA, B, SFB, C2, M=p.M, N=p.N, K=p.K)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(C2), bits(outs[i][0])), "pair and ticket sums differ, call %d" % i
+    group = [(80, 2048, 4096), (40, 2048, 4096), (3, 256, 4096)]
+    ginfo, _ = lib.group_gemm_plan(group)
+    assert (ginfo["tile_n"], ginfo["split_k"]) == (64, 2)
+    gprobs = inputs.draw_problems(7710, group)
+    for i, (p, got) in enumerate(zip(gprobs, run_group(lib, gprobs))):
+        check_against_full_oracle(got, p, "two-slice group %d" % i)
+
+
 # ------------------------------------------------------------------ grouped GEMM
 
 def run_group(lib, probs):
