@@ -439,15 +439,21 @@ def test_two_slice_pairs_across_interleaved_calls(lib):
     empty state.  On one stream: a two-slice panel call, a two-slice stream
     call (ticket protocol), a wide-tile call whose K split uses the partial
     tiles after the pair slots, the same two-slice calls again on new data,
-    and a two-slice grouped panel call; each against the oracle, and the
+    a two-slice panel call whose slices run on different XCDs, and a
+    two-slice grouped panel call; each against the oracle, and the
     repeated calls bitwise equal to the allocation-free entry point's sums
     (which keeps no pair slots and takes the ticket protocol)."""
     panel, stream_, wide = (100, 3072, 4096), (33, 2400, 2048), (2304, 4096, 1024)
-    assert (lib.gemm_plan(*panel)["tile_n"], lib.gemm_plan(*panel)["split_k"]) == (64, 2)
-    assert (lib.gemm_plan(*stream_)["tile_n"], lib.gemm_plan(*stream_)["split_k"]) == (32, 2)
+    # 98 tiles, 196 workgroups: not a multiple of the eight XCDs, so the two
+    # slices of a tile run on neighbouring XCDs (the pairs meet across L2s)
+    cross = (100, 3104, 4096)
+    for shape, tile_n in ((panel, 64), (cross, 64), (stream_, 32)):
+        info = lib.gemm_plan(*shape)
+        assert (info["tile_n"], info["split_k"]) == (tile_n, 2), shape
+    assert lib.gemm_plan(*cross)["workgroups"] % 8 != 0
     info = lib.gemm_plan(*wide)
     assert info["kernel"] == 4 and info["split_k"] > 1
-    seq = [panel, stream_, wide, panel, stream_]
+    seq = [panel, stream_, wide, panel, stream_, cross]
     probs = inputs.draw_problems(7700, seq)
     outs = []
     for p in probs:
@@ -461,7 +467,7 @@ def test_two_slice_pairs_across_interleaved_calls(lib):
             check_against_full_oracle(bits(C), p, what)
         else:
             check_sampled(bits(C), p, 7701 + i, what, plan_tile(lib, p.M, p.N, p.K))
-    for i in (3, 4):
+    for i in (3, 4, 5):
         p = probs[i]
         A, SFA, B, SFB = outs[i][1]
         C2 = poisoned(p.M, p.N)
