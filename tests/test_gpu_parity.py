@@ -942,15 +942,19 @@ def test_group_gemm_device_table_in_graph(lib):
             assert_parity(got[:m], c16, bound, "graph replay M=%s group %d" % (ms, g_))
 
 
-def test_k_split_gemm_under_stream_capture(lib):
+@pytest.mark.parametrize("M,N,K,tile_n,split", [
+    (64, 1024, 8192, 32, 8),    # stream tile, eight slices (ticket protocol)
+    (100, 3072, 4096, 64, 2),   # panel tile, two slices (pair slots)
+])
+def test_k_split_gemm_under_stream_capture(lib, M, N, K, tile_n, split):
     """A K-split call needs its stream's workspace.  Captured on a stream that
     has none yet it is refused (NOT_SUPPORTED, nothing enqueued); after one
     eager call on that stream the same call captures, and every replay of the
-    graph (eager work and synchronisations between them) matches the oracle."""
-    M, N, K = 64, 1024, 8192
+    graph (eager work and synchronisations between them) matches the oracle,
+    so each replay leaves the counters and pair slots as it found them."""
     info = lib.gemm_plan(M, N, K)
-    assert info["split_k"] > 1 and info["workspace_bytes"] > 0
-    p = inputs.draw_problems(6100, [(M, N, K)])[0]
+    assert (info["tile_n"], info["split_k"]) == (tile_n, split) and info["workspace_bytes"] > 0
+    p = inputs.draw_problems(6100 + split, [(M, N, K)])[0]
     A, SFA, B, SFB, C = dev_problem(p)
     torch.cuda.synchronize()
     assert lib.release_workspaces() is None  # no stream has a workspace now
