@@ -329,28 +329,32 @@ __device__ inline bool add_slices(float (&v)[kN], float *part, int slice_elems, 
 }
 
 // Two-slice sum without a ticket (split_k == 2 and pair slots given).  Each
-// thread exchanges each of its kN values into its slot (slot + i * kStride),
-// which holds kPairSentinel until the first of the two slices' exchanges.
-// The exchange that gets a value back is the second one for that element: it
-// adds the two (fp32 addition of two terms is commutative, so the sum does not
-// depend on which slice comes second and equals the slice-ordered sum),
-// restores the sentinel for the next launch, and marks the element as this
-// thread's to write.  The pairing rests only on the atomicity of the two
-// exchanges of one slot (agent scope): the second reads the first's value.
+// thread holds kN pairs of horizontally adjacent outputs, lo[i] and hi[i],
+// and exchanges each pair (one 64-bit agent-scope atomic exchange) into its
+// slot, slot + i * kStride pairs; between launches every slot holds
+// kPairSentinel in both halves.  The exchange that gets a value back is the
+// second one for that pair: it adds the two (fp32 addition of two terms is
+// commutative, so the sum does not depend on which slice comes second and
+// equals the slice-ordered sum), restores the sentinel for the next launch,
+// and marks the pair as this thread's to write.  The pairing rests only on
+// the atomicity of the two exchanges of one slot.
 template <int kN, int kStride>
-__device__ inline void add_pair(float (&v)[kN], bool (&own)[kN], uint32_t *slot)
+__device__ inline void add_pair(float (&lo)[kN], float (&hi)[kN], bool (&own)[kN], uint64_t *slot)
 {
-    uint32_t old[kN];
+    constexpr uint64_t kEmpty = ((uint64_t)kPairSentinel << 32) | kPairSentinel;
+    uint64_t old[kN];
 #pragma unroll
     for (int i = 0; i < kN; ++i)
-        old[i] = __hip_atomic_exchange(slot + i * kStride, __float_as_uint(v[i]), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+        old[i] = __hip_atomic_exchange(slot + i * kStride,
+                                       ((uint64_t)__float_as_uint(hi[i]) << 32) | __float_as_uint(lo[i]),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
-        own[i] = old[i] != kPairSentinel;
+        own[i] = old[i] != kEmpty;
         if (own[i]) {
-            v[i] += __uint_as_float(old[i]);
-            __hip_atomic_store(slot + i * kStride, kPairSentinel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lo[i] += __uint_as_float((uint32_t)old[i]);
+            hi[i] += __uint_as_float((uint32_t)(old[i] >> 32));
+            __hip_atomic_store(slot + i * kStride, kEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -678,6 +682,8 @@ struct PanelSlot {
 // takes a ticket from the tile's counter; the last to arrive adds all
 // partial tiles in slice order (so the result does not depend on arrival
 // order), writes C and resets the counter to zero for the next launch.
+// With split_k == 2 and pair slots the two slices meet in the slots instead
+// (add_pair), with no ticket or fence.
 template <bool kVec, int kMB, bool kBlocked>
 __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable tab, float *partials, int *counters)
 {
@@ -931,43 +937,62 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
                     (float4){acc[oa][ob][4 * g], acc[oa][ob][4 * g + 1], acc[oa][ob][4 * g + 2], acc[oa][ob][4 * g + 3]};
     __syncthreads();
 
-    // thread -> column n = tid % 64, rows 8 (tid / 64) .. + 7, summed in wave order
-    const int n = tid & 63, m0 = (tid >> 6) * 8;
-    float v[8];
+    // thread -> columns n, n + 1 (n = 2 (tid % 32)), rows 4 (tid / 32) .. + 3,
+    // summed in wave order: lo[r], hi[r] are row m0 + r of columns n, n + 1
+    const int n = (tid & 31) * 2, m0 = (tid >> 5) * 4;
+    float lo[4], hi[4];
     {
         const float4 p = *(const float4 *)(red + n * kColStride + m0);
-        const float4 q = *(const float4 *)(red + n * kColStride + m0 + 4);
-        v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
-        v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+        const float4 q = *(const float4 *)(red + (n + 1) * kColStride + m0);
+        lo[0] = p.x; lo[1] = p.y; lo[2] = p.z; lo[3] = p.w;
+        hi[0] = q.x; hi[1] = q.y; hi[2] = q.z; hi[3] = q.w;
     }
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) {
         const float4 p = *(const float4 *)(red + w * kWaveFloats + n * kColStride + m0);
-        const float4 q = *(const float4 *)(red + w * kWaveFloats + n * kColStride + m0 + 4);
-        v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
-        v[4] += q.x; v[5] += q.y; v[6] += q.z; v[7] += q.w;
+        const float4 q = *(const float4 *)(red + w * kWaveFloats + (n + 1) * kColStride + m0);
+        lo[0] += p.x; lo[1] += p.y; lo[2] += p.z; lo[3] += p.w;
+        hi[0] += q.x; hi[1] += q.y; hi[2] += q.z; hi[3] += q.w;
     }
-    bool own[8]; // the elements this thread writes
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        own[i] = true;
+    bool own[4] = {true, true, true, true}; // the pairs this thread writes
     if (S == 2 && tab.pairs != nullptr) {
-        // pair slots, row-major [tile][64][64]
-        add_pair<8, BN>(v, own, tab.pairs + (long)tile * kTileElems + m0 * BN + n);
+        // pair slots, row-major [tile][64][64] floats, one 64-bit slot per
+        // two adjacent columns
+        add_pair<4, BN / 2>(lo, hi, own, (uint64_t *)(tab.pairs + (long)tile * kTileElems + m0 * BN + n));
     } else if (S > 1) {
-        // row-major partial tiles, [tile][slice][64][64]
-        if (!add_slices<8, BN>(v, partials + (long)tile * S * kTileElems + m0 * BN + n, kTileElems, S, split,
-                               counters + tile, &s_last))
+        // partial tiles [tile][slice][8][kThreads]: value i of thread t at
+        // i * kThreads + t
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (!add_slices<8, kThreads>(v, partials + (long)tile * S * kTileElems + tid, kTileElems, S, split,
+                                     counters + tile, &s_last))
             return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            lo[r] = v[r];
+            hi[r] = v[4 + r];
+        }
     }
     const int col = col0 + n;
     if (col >= N)
         return;
+    // two adjacent outputs as one 4-byte store where both lie inside N and
+    // the address is 4-byte aligned
+    const bool pair_store = col + 1 < N && (N & 1) == 0 && (((uintptr_t)d.C) & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = row0 + m0 + i;
-        if (own[i] && row < M)
-            d.C[(long)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v[i]);
+    for (int r = 0; r < 4; ++r) {
+        const int row = row0 + m0 + r;
+        if (!own[r] || row >= M)
+            continue;
+        uint16_t *dst = d.C + (long)row * N + col;
+        const uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)lo[r]);
+        const uint16_t b = __builtin_bit_cast(uint16_t, (_Float16)hi[r]);
+        if (pair_store) {
+            *(uint32_t *)dst = (uint32_t)a | ((uint32_t)b << 16);
+        } else {
+            dst[0] = a;
+            if (col + 1 < N)
+                dst[1] = b;
+        }
     }
 }
 
