@@ -355,3 +355,25 @@ def test_plan_wide_tile_needs_a_tile_per_cu():
     info = g.gemm_plan(2048, 2048, 2048)
     assert info["kernel"] == 3 and info["tile_n"] == 128
     assert g.gemm_plan(4096, 2048, 2048)["kernel"] == 4  # 256 wide tiles
+
+
+def test_two_slice_panel_plans_fit_the_pair_slots():
+    """Two-slice launches of the 64 x 64 panel tile sum through the library
+    workspace's pair slots, one 32-bit word per output element of at most 128
+    tiles (2 MiB between the tile counters and the partial tiles).  Over seeded
+    random single and grouped shapes in the 64-row regimes, every such plan
+    stays within 128 tiles and asks for the counters, the pair slots and two
+    16 KiB partial tiles per tile."""
+    rng = np.random.default_rng(77)
+    pair_bytes = 128 * 64 * 64 * 4
+    seen = 0
+    for _ in range(400):
+        G = int(rng.integers(1, 4))
+        shapes = [(int(rng.integers(1, 400)), int(rng.integers(1, 9000)), 256 * int(rng.integers(1, 64)))
+                  for _ in range(G)]
+        info, _ = g.group_gemm_plan(shapes)
+        if info["kernel"] == 2 and info["tile_n"] == 64 and info["split_k"] == 2:
+            seen += 1
+            assert info["total_tiles"] <= 128, shapes
+            assert info["workspace_bytes"] == 16384 + pair_bytes + info["total_tiles"] * 2 * 64 * 64 * 4
+    assert seen >= 10  # the sweep reaches the two-slice panel plans
