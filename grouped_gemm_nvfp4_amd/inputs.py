@@ -7,11 +7,12 @@ consume what it returns.
 Recipe (stated once, used everywhere):
   * ``rng = numpy.random.default_rng(seed)``; the named workloads below use
     ``seed = 1000 + index`` in the order they are listed.
-  * Packed operands: every byte uniform over 0..255, i.e. two independent
-    uniform e2m1 codes per byte (all 16 codes, including both zeros).
+  * Operands: e2m1 codes uniform over all 16 (both zeros included), drawn
+    as a [rows][K] array and packed two per byte along K, the even K index
+    in the low nibble: byte j of a row = code[2j] | code[2j + 1] << 4.
   * Scales: uniform over the 49 e4m3fn codes 0x20..0x50, the finite positive
     codes whose values lie in [0.125, 8].
-  * Draw order, per group in order: A bytes [M][K/2], B bytes [N][K/2],
+  * Draw order, per group in order: A codes [M][K], B codes [N][K],
     SFA codes [M][K/16], SFB codes [N][K/16].  The 8-group MoE-like workload
     first draws its per-group M from {64, 128, ..., 512}.
 
@@ -49,13 +50,20 @@ class Problem:
                     B=self.B, SFB=self.SFB)
 
 
+def _packed_codes(rng: np.random.Generator, rows: int, K: int) -> np.ndarray:
+    """rows x K uniform 4-bit codes, packed two per byte along K (even index
+    in the low nibble): uint8 [rows][K/2]."""
+    codes = rng.integers(0, 16, size=(rows, K), dtype=np.uint8)
+    return np.ascontiguousarray(codes[:, 0::2] | (codes[:, 1::2] << 4))
+
+
 def draw_problem(rng: np.random.Generator, M: int, N: int, K: int,
                  scale_codes: np.ndarray = SCALE_CODES) -> Problem:
     """Draw one problem's operands in the recipe's order."""
     if K % 16 != 0:
         raise ValueError("K must be a multiple of 16 (one scale per 16 elements)")
-    A = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
-    B = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    A = _packed_codes(rng, M, K)
+    B = _packed_codes(rng, N, K)
     SFA = rng.choice(scale_codes, size=(M, K // 16)).astype(np.uint8)
     SFB = rng.choice(scale_codes, size=(N, K // 16)).astype(np.uint8)
     return Problem(M, N, K, A, SFA, B, SFB)
