@@ -482,6 +482,31 @@ def test_two_slice_pairs_across_interleaved_calls(lib):
         check_against_full_oracle(got, p, "two-slice group %d" % i)
 
 
+def test_two_slice_pairs_repeat_bitwise(lib):
+    """Twelve calls alternating two two-slice panel products (one with its
+    slices on different XCDs) and a ticket-summed stream product on one
+    stream, C poisoned before each: the first call of each product matches
+    the oracle, and every later call's C is bitwise the first call's (the pair
+    slots return to their empty state after every launch, whatever ran
+    before)."""
+    shapes = [(64, 7168, 16384), (100, 3104, 4096), (33, 2400, 2048)]
+    probs = inputs.draw_problems(7720, shapes)
+    devs = [dev_problem(p) for p in probs]
+    first = [None] * len(shapes)
+    for call in range(12):
+        i = call % len(shapes)
+        p, (A, SFA, B, SFB, C) = probs[i], devs[i]
+        C.fill_(-1)
+        lib.nvfp4_gemm(A, SFA, B, SFB, C, M=p.M, N=p.N, K=p.K)
+        torch.cuda.synchronize()
+        got = bits(C)
+        if first[i] is None:
+            check_against_full_oracle(got, p, "first call %dx%dx%d" % (p.M, p.N, p.K))
+            first[i] = got
+        else:
+            assert np.array_equal(got, first[i]), "call %d differs, %dx%dx%d" % (call, p.M, p.N, p.K)
+
+
 # ------------------------------------------------------------------ grouped GEMM
 
 def run_group(lib, probs):
