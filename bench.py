@@ -544,7 +544,7 @@ def main(argv=None):
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     pow2 = args.scales == "pow2"
