@@ -76,7 +76,7 @@ def _fake_timing(kern_us):
 
 
 def test_output_line_carries_every_field():
-    """The JSON line of a run: the driver's contract, the roofline and CPU
+    """The JSON line of a run: the benchmark line's fields, the roofline and CPU
     baseline objects, the other workloads and the system metadata."""
     args = bench.parse(["--steps", "20", "--warmup", "5"])
     heads = {}
