@@ -507,6 +507,61 @@ def test_two_slice_pairs_repeat_bitwise(lib):
             assert np.array_equal(got, first[i]), "call %d differs, %dx%dx%d" % (call, p.M, p.N, p.K)
 
 
+HIP_STREAM_PER_THREAD = 2  # hipStreamPerThread in hip_runtime_api.h
+
+
+@pytest.mark.parametrize("streams", ["own", "per-thread"])
+def test_concurrent_streams_keep_their_own_workspaces(lib, streams):
+    """Two host threads issue K-split calls at the same time, each on a
+    stream of its own (a torch stream each, or hipStreamPerThread, which names
+    a different stream in every thread): two-slice panel calls (pair slots), a
+    ticket-summed stream call and a wide-tile balancing split.  Every output
+    is bitwise the one a serial run on the default stream gives, so the two
+    streams never share tile counters, pair slots or partial tiles."""
+    import threading
+    from grouped_gemm_nvfp4_amd import _binding as b
+    shapes = [(100, 3072, 4096), (64, 7168, 16384), (64, 1024, 8192), (2304, 4096, 1024)]
+    splits = [lib.gemm_plan(*sh)["split_k"] for sh in shapes]
+    assert splits[0] == 2 and splits[1] == 2 and min(splits) > 1
+    probs = inputs.draw_problems(7730, shapes)
+    devs = [dev_problem(p) for p in probs]
+    ref = []
+    for p, (A, SFA, B, SFB, C) in zip(probs, devs):
+        lib.nvfp4_gemm(A, SFA, B, SFB, C, M=p.M, N=p.N, K=p.K)
+        torch.cuda.synchronize()
+        ref.append(bits(C))
+    iters = 3
+    outs = [[[poisoned(p.M, p.N) for p in probs] for _ in range(iters)] for _ in range(2)]
+    torch_streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(t):
+        try:
+            handle = HIP_STREAM_PER_THREAD if streams == "per-thread" else torch_streams[t].cuda_stream
+            for it in range(iters):
+                for p, (A, SFA, B, SFB, _), C in zip(probs, devs, outs[t][it]):
+                    rc = b.raw_gemm(A.data_ptr(), SFA.data_ptr(), B.data_ptr(), SFB.data_ptr(), C.data_ptr(),
+                                    p.M, p.N, p.K, handle)
+                    if rc != b.NVFP4_OK:
+                        errors.append((t, it, rc))
+        except Exception as e:  # reported below, on the main thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t in range(2):
+        for it in range(iters):
+            for i, p in enumerate(probs):
+                assert np.array_equal(bits(outs[t][it][i]), ref[i]), \
+                    "thread %d call %d %dx%dx%d differs" % (t, it, p.M, p.N, p.K)
+
+
 # ------------------------------------------------------------------ grouped GEMM
 
 def run_group(lib, probs):
