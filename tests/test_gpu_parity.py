@@ -482,6 +482,28 @@ def test_two_slice_pairs_across_interleaved_calls(lib):
         check_against_full_oracle(got, p, "two-slice group %d" % i)
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (100, 3071, 4096),   # odd N: two-byte stores, the last pair's second column past N
+    (20, 7167, 16384),   # M <= 32 (one row block) and odd N
+    (1, 7001, 16384),    # a single row; 220 workgroups, not a multiple of 8
+])
+def test_two_slice_pairs_ragged_edges(lib, M, N, K):
+    """Two-slice panel launches at ragged edges: every output against the
+    oracle and bitwise the allocation-free entry point's ticket sums."""
+    info = lib.gemm_plan(M, N, K)
+    assert (info["tile_n"], info["split_k"]) == (64, 2)
+    p = inputs.draw_problems(7740 + M, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    got = bits(C)
+    check_against_full_oracle(got, p, "two-slice %dx%dx%d" % (M, N, K))
+    C2 = poisoned(M, N)
+    lib.nvfp4_gemm_noalloc(A, SFA, B, SFB, C2, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(C2), got), "pair and ticket sums differ"
+
+
 def test_two_slice_pairs_repeat_bitwise(lib):
     """Twelve calls alternating two two-slice panel products (one with its
     slices on different XCDs) and a ticket-summed stream product on one
