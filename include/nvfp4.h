@@ -31,9 +31,10 @@
  * Threads: the calls may be made from several threads.  Calls that split K
  * use a device workspace that the library keeps per (device, stream) pair
  * (per calling thread as well for hipStreamPerThread) and grows on demand
- * (hipMalloc plus a clear of its tile counters, both outside the enqueued
- * work); calls on one stream are ordered by that stream, so they never share
- * a workspace concurrently.
+ * (hipMalloc plus one initialisation of its tile counters and two-slice
+ * pair slots, enqueued on the stream before the call's kernels; every call
+ * leaves them as it found them); calls on one stream are ordered by that
+ * stream, so they never share a workspace concurrently.
  *
  * Stream capture: a call that would have to allocate or grow its stream's
  * workspace while that stream is capturing returns NVFP4_ERROR_NOT_SUPPORTED
