@@ -557,7 +557,8 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(GroupTable tab, float 
         SCHED_FENCE();
         for (int t = kt0; t < kt1; t += 2) {
             step(t, x0);
-            step(t + 1, x1);
+            if (t + 1 < kt1)
+                step(t + 1, x1);
         }
     }
 
@@ -684,7 +685,13 @@ struct PanelSlot {
 // order), writes C and resets the counter to zero for the next launch.
 // With split_k == 2 and pair slots the two slices meet in the slots instead
 // (add_pair), with no ticket or fence.
-template <bool kVec, int kMB, bool kBlocked>
+//
+// kTail: some wave's count of K tiles is not a multiple of four, so the
+// trips of four tiles end early; the staging writes and loads of the steps
+// past a wave's last tile are skipped.  Launches whose every wave runs whole
+// trips take the form without these checks (its schedule is the faster one
+// there).
+template <bool kVec, int kMB, bool kBlocked, bool kTail>
 __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable tab, float *partials, int *counters)
 {
     static_assert(kMB == 1 || kMB == 2, "one or two 32-row blocks");
@@ -895,14 +902,24 @@ __global__ __launch_bounds__(panel::kThreads) void gemm_panel_kernel(GroupTable 
         else
             load_bytes(kt0);
         SCHED_FENCE();
-        // four K tiles per trip, one per scale-group slot; steps past kt1 only
-        // move zeros (their loads are out of range) and skip the compute
+        // four K tiles per trip, one per scale-group slot; steps past kt1 skip
+        // the compute (and with kTail the staging and the next load)
         for (int t = kt0; t < kt1; t += 4) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                put(x, u);
+                if constexpr (kTail) {
+                    if (t + u < kt1)
+                        put(x, u);
+                } else {
+                    put(x, u);
+                }
                 SCHED_FENCE();
-                load(x, t + u + 1);
+                if constexpr (kTail) {
+                    if (t + u + 1 < kt1)
+                        load(x, t + u + 1);
+                } else {
+                    load(x, t + u + 1);
+                }
                 if (kBlocked) {
                     if (u == 3)
                         load_atoms(t + 4);
@@ -1093,6 +1110,20 @@ hipError_t launch_clear_words(void *p, int words, hipStream_t stream)
     return hipLaunchKernel((const void *)clear_words_kernel, dim3(1), dim3(256), args, 0, stream);
 }
 
+// True when some wave of a panel launch has a K-tile count that is not a
+// multiple of four: a slice of L K tiles gives its eight waves L (w + 1) / 8
+// - L w / 8 tiles each, all multiples of four exactly when L % 32 == 0.
+bool panel_tail(const GroupTable &table)
+{
+    const int S = table.split_k;
+    for (int g = 0; g < table.num_groups; ++g) {
+        const int nkt = (table.g[g].K + panel::BK - 1) / panel::BK;
+        if (nkt % S != 0 || (nkt / S) % (4 * panel::kWaves) != 0)
+            return true;
+    }
+    return false;
+}
+
 hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, int *counters, float *partials,
                           hipStream_t stream)
 {
@@ -1124,8 +1155,18 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, int *counters
         bool half = true;
         for (int g = 0; g < table.num_groups; ++g)
             half = half && table.g[g].M <= 32;
-        const void *fn = half ? (vec ? (const void *)gemm_panel_kernel<true, 1, false> : (const void *)gemm_panel_kernel<false, 1, false>)
-                              : (vec ? (const void *)gemm_panel_kernel<true, 2, false> : (const void *)gemm_panel_kernel<false, 2, false>);
+        const bool tail = panel_tail(table);
+        const void *fn;
+        if (tail)
+            fn = half ? (vec ? (const void *)gemm_panel_kernel<true, 1, false, true>
+                             : (const void *)gemm_panel_kernel<false, 1, false, true>)
+                      : (vec ? (const void *)gemm_panel_kernel<true, 2, false, true>
+                             : (const void *)gemm_panel_kernel<false, 2, false, true>);
+        else
+            fn = half ? (vec ? (const void *)gemm_panel_kernel<true, 1, false, false>
+                             : (const void *)gemm_panel_kernel<false, 1, false, false>)
+                      : (vec ? (const void *)gemm_panel_kernel<true, 2, false, false>
+                             : (const void *)gemm_panel_kernel<false, 2, false, false>);
         return hipLaunchKernel(fn, dim3(total), dim3(panel::kThreads), args, 0, stream);
     }
     case kStream64x32Blocked: {
@@ -1144,7 +1185,11 @@ hipError_t launch_grouped(const GroupTable &table, TileConfig cfg, int *counters
                 return hipErrorInvalidValue;
             half = half && table.g[g].M <= 32;
         }
-        const void *fn = half ? (const void *)gemm_panel_kernel<true, 1, true> : (const void *)gemm_panel_kernel<true, 2, true>;
+        const bool tail = panel_tail(table);
+        const void *fn = tail ? (half ? (const void *)gemm_panel_kernel<true, 1, true, true>
+                                      : (const void *)gemm_panel_kernel<true, 2, true, true>)
+                              : (half ? (const void *)gemm_panel_kernel<true, 1, true, false>
+                                      : (const void *)gemm_panel_kernel<true, 2, true, false>);
         return hipLaunchKernel(fn, dim3(total), dim3(panel::kThreads), args, 0, stream);
     }
     case kTile128x128K4:
