@@ -504,6 +504,34 @@ def test_two_slice_pairs_ragged_edges(lib, M, N, K):
     assert np.array_equal(bits(C2), got), "pair and ticket sums differ"
 
 
+@pytest.mark.parametrize("M,N,K,split", [
+    (64, 7168, 4096, 2),    # one K tile per wave: each wave's trip ends after one step
+    (24, 7168, 8192, 2),    # the one-row-block form, two tiles per wave
+    (17, 4096, 12800, 4),   # 50 K tiles in four slices of 12 or 13: uneven trips, ticket sums
+    (48, 7000, 6016, 2),    # K % 256 != 0: byte-wise scales, a ragged last K tile
+])
+def test_panel_tail_form(lib, M, N, K, split):
+    """Panel launches whose waves' K-tile counts are not multiples of four
+    take the form that stops each wave's last trip at its last tile: every
+    output against the oracle, and (K % 256 == 0) blocked scales bitwise the
+    plain call."""
+    info = lib.gemm_plan(M, N, K)
+    nkt = (K + 255) // 256
+    assert (info["tile_n"], info["split_k"]) == (64, split)
+    assert nkt % split != 0 or (nkt // split) % 32 != 0
+    p = inputs.draw_problems(7750 + M, [(M, N, K)])[0]
+    A, SFA, B, SFB, C = dev_problem(p)
+    lib.nvfp4_gemm(A, SFA, B, SFB, C, M=M, N=N, K=K)
+    torch.cuda.synchronize()
+    got = bits(C)
+    check_against_full_oracle(got, p, "panel tail %dx%dx%d" % (M, N, K))
+    if K % 256 == 0:
+        C2 = poisoned(M, N)
+        lib.nvfp4_gemm_blocked(A, blocked_dev(p.SFA, M, K), B, blocked_dev(p.SFB, N, K), C2, M, N, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(C2), got), "blocked scales change C"
+
+
 def test_two_slice_pairs_repeat_bitwise(lib):
     """Twelve calls alternating two two-slice panel products (one with its
     slices on different XCDs) and a ticket-summed stream product on one
